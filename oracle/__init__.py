@@ -1,0 +1,120 @@
+"""CPU oracle for C = A * B (float32 inputs, double accumulation).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it; the library never does. It is a thin ctypes wrapper
+over ``oracle.c`` (plain C, gcc, OpenMP), which shares no code with the GPU
+path. The arithmetic and its citations are in ``oracle.c``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = LIB_PATH, extra_flags=()) -> str:
+    """Compile the oracle with gcc into a shared library; returns its path."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+           "-std=c11", "-Wall", "-Wextra", "-Werror", *extra_flags, src,
+           "-o", out + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64]
+    lib.oracle_gemm.restype = ctypes.c_int
+    lib.oracle_gemm_entries.argtypes = [i64, vp, vp, i64, vp, i64, vp, i64, vp, vp]
+    lib.oracle_gemm_entries.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the compiled oracle, building it first if no library exists."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _rows_view(x: np.ndarray, rows: int, cols: int):
+    """(pointer, leading dimension) of a row-major float32 matrix view."""
+    if x.dtype != np.float32:
+        raise TypeError("oracle inputs must be float32")
+    if x.ndim != 2 or x.shape[0] < rows or x.shape[1] < cols:
+        raise ValueError("operand smaller than its logical shape")
+    if rows == 0 or cols == 0:
+        return x.ctypes.data, max(cols, 1)
+    if x.strides[1] != 4 or x.strides[0] % 4:
+        raise ValueError("operand must be row-major with unit column stride")
+    return x.ctypes.data, x.strides[0] // 4
+
+
+def gemm(A: np.ndarray, B: np.ndarray, with_abs: bool = False, lib=None):
+    """C = A @ B in double (and S = |A| @ |B| if ``with_abs``).
+
+    A is M x K, B is K x N, row-major float32 (views with a row stride larger
+    than the row length are accepted and read through their leading dimension).
+    """
+    lib = lib or load()
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    pa, lda = _rows_view(A, M, K)
+    pb, ldb = _rows_view(B, K, N)
+    C = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64) if with_abs else None
+    rc = lib.oracle_gemm(M, N, K, pa, max(lda, 1), pb, max(ldb, 1),
+                         C.ctypes.data, max(N, 1),
+                         S.ctypes.data if with_abs else None, max(N, 1))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm returned {rc}")
+    return (C, S) if with_abs else C
+
+
+def gemm_entries(A: np.ndarray, B: np.ndarray, rows, cols, lib=None):
+    """(C[rows[e], cols[e]], S[rows[e], cols[e]]) for each e, in double."""
+    lib = lib or load()
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape or rows.ndim != 1:
+        raise ValueError("rows and cols must be 1-D and of equal length")
+    if rows.size and (rows.min() < 0 or rows.max() >= M
+                      or cols.min() < 0 or cols.max() >= N):
+        raise IndexError("entry outside the product")
+    pa, lda = _rows_view(A, M, K)
+    pb, ldb = _rows_view(B, K, N)
+    out = np.empty(rows.size, dtype=np.float64)
+    sabs = np.empty(rows.size, dtype=np.float64)
+    rc = lib.oracle_gemm_entries(rows.size, rows.ctypes.data, cols.ctypes.data,
+                                 K, pa, max(lda, 1), pb, max(ldb, 1),
+                                 out.ctypes.data, sabs.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_entries returned {rc}")
+    return out, sabs
+
+
+def num_threads(lib=None) -> int:
+    return (lib or load()).oracle_num_threads()

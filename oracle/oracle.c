@@ -1,0 +1,100 @@
+/*
+ * CPU oracle for the FP32 matrix product C = A * B.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the library calls this; only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg load it. It
+ * shares no source with the GPU path.
+ *
+ * Definition followed ("Shared Memory Tiling for Matrix Multiplication",
+ * opening definition; "Matrix Multiplication -- Naive to Tiled", section 02):
+ *     C[i][j] = sum over k = 0 .. K-1 of A[i][k] * B[k][j]
+ * with A of M x K, B of K x N, C of M x N, all stored row-major; a leading
+ * dimension gives the distance in elements between consecutive rows.
+ *
+ * Precision: every product and partial sum is formed in double, and each
+ * C[i][j] is summed in ascending k, exactly as the textbook triple loop does
+ * it. The loops are written i, k, j: that only changes which element is
+ * worked on next, never the order of the terms of any one element, so the
+ * result is bit-for-bit the i, j, k loop's. The rows are shared among OpenMP
+ * threads; each element is still summed by one thread in ascending k.
+ *
+ * Alongside C the oracle can return S[i][j] = sum_k |A[i][k]| * |B[k][j]|,
+ * which scales the elementwise error bound of a float32 result.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math: the sums must not
+ * be reassociated).
+ */
+#include <stdint.h>
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double absd(double x) { return x < 0.0 ? -x : x; }
+
+/* Full product. C (and S, when not NULL) receive M x N doubles with leading
+ * dimension ldc (lds). Returns 0, or -1 on a negative size. */
+int oracle_gemm(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                double *C, int64_t ldc,
+                double *S, int64_t lds)
+{
+    if (M < 0 || N < 0 || K < 0) return -1;
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *c = C + i * ldc;
+        double *s = S ? S + i * lds : NULL;
+        for (int64_t j = 0; j < N; ++j) c[j] = 0.0;
+        if (s)
+            for (int64_t j = 0; j < N; ++j) s[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = (double)A[i * lda + k];
+            const float *b = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j) c[j] += a * (double)b[j];
+            if (s) {
+                const double aa = absd(a);
+                for (int64_t j = 0; j < N; ++j) s[j] += aa * absd((double)b[j]);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Selected elements only: out[e] = C[rows[e]][cols[e]] (and sabs[e] = S[..]
+ * when sabs is not NULL), each summed in ascending k like oracle_gemm. For
+ * checking a few outputs of a product too large to form on the CPU. */
+int oracle_gemm_entries(int64_t n, const int64_t *rows, const int64_t *cols,
+                        int64_t K,
+                        const float *A, int64_t lda,
+                        const float *B, int64_t ldb,
+                        double *out, double *sabs)
+{
+    if (n < 0 || K < 0) return -1;
+    int64_t e;
+#pragma omp parallel for schedule(static)
+    for (e = 0; e < n; ++e) {
+        const int64_t i = rows[e], j = cols[e];
+        double acc = 0.0, accabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = (double)A[i * lda + k];
+            const double b = (double)B[k * ldb + j];
+            acc += a * b;
+            accabs += absd(a) * absd(b);
+        }
+        out[e] = acc;
+        if (sabs) sabs[e] = accabs;
+    }
+    return 0;
+}
+
+/* Number of OpenMP threads a parallel region of the oracle will use. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

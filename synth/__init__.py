@@ -1,0 +1,113 @@
+"""Seeded synthetic matrices for the FP32 GEMM tests and benchmark.
+
+This module only draws numbers; it holds none of the product's arithmetic, so
+both the HIP path's callers and the CPU oracle's callers can take their inputs
+from here without sharing any GEMM code.
+
+Generator: SplitMix64 (G. L. Steele, D. Lea, C. H. Flood, "Fast splittable
+pseudorandom number generators", OOPSLA 2014), used counter-style: element i of
+a stream with seed s is mix(s + (i + 1) * GAMMA), where GAMMA is the 64-bit
+golden-ratio increment and mix() is the published finaliser
+(xor-shift 30 / multiply / xor-shift 27 / multiply / xor-shift 31). This is the
+same sequence the sequential generator produces from state s, but any element
+can be drawn on its own, so a sub-block of a large matrix is reproducible
+without generating the rest.
+
+Value maps (all results are exactly representable in float32):
+
+* ``uniform01``  -- the top 24 bits u of each draw, value u * 2**-24, in [0, 1).
+* ``uniform_pm1`` -- (u - 2**23) * 2**-23, in [-1, 1).
+* ``small_int``  -- integers in [lo, hi] from the top 32 bits (modulo map).
+
+The pages seed a uniform generator (P1 "Naive Implementation": seed 42 and
+rand()/RAND_MAX over [0, 1]; "From 306 ms to 86 ms", "How each kernel was
+timed": the same seeded random matrices for every kernel). glibc's rand() is
+not portable, so the distribution is kept and the generator replaced; the
+2**-24 grid keeps every product of two inputs exact in double precision.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GAMMA = 0x9E3779B97F4A7C15
+MIX1 = 0xBF58476D1CE4E5B9
+MIX2 = 0x94D049BB133111EB
+MASK64 = (1 << 64) - 1
+
+# Seeds used for the A and B operands of every configuration.
+SEED_A = 42
+SEED_B = 43
+
+
+def splitmix64_scalar(seed: int, index: int) -> int:
+    """Element ``index`` (0-based) of the SplitMix64 stream seeded with ``seed``,
+    in plain Python integers (the definition, used to pin the vector form)."""
+    z = (seed + (index + 1) * GAMMA) & MASK64
+    z = ((z ^ (z >> 30)) * MIX1) & MASK64
+    z = ((z ^ (z >> 27)) * MIX2) & MASK64
+    return z ^ (z >> 31)
+
+
+def splitmix64(seed: int, n: int, offset: int = 0) -> np.ndarray:
+    """Elements ``offset .. offset+n-1`` of the stream, as uint64 (wrapping)."""
+    with np.errstate(over="ignore"):
+        i = np.arange(offset + 1, offset + n + 1, dtype=np.uint64)
+        z = np.uint64(seed & MASK64) + i * np.uint64(GAMMA)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(MIX1)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(MIX2)
+        return z ^ (z >> np.uint64(31))
+
+
+def _top24(seed: int, shape) -> np.ndarray:
+    n = int(np.prod(shape, dtype=np.int64))
+    return (splitmix64(seed, n) >> np.uint64(40)).reshape(shape)
+
+
+def uniform01(seed: int, shape) -> np.ndarray:
+    """float32 matrix with i.i.d. entries u * 2**-24, u uniform on [0, 2**24)."""
+    u = _top24(seed, shape).astype(np.float64)
+    return (u * 2.0**-24).astype(np.float32)
+
+
+def uniform_pm1(seed: int, shape) -> np.ndarray:
+    """float32 matrix with i.i.d. entries (u - 2**23) * 2**-23 in [-1, 1)."""
+    u = _top24(seed, shape).astype(np.int64) - (1 << 23)
+    return (u.astype(np.float64) * 2.0**-23).astype(np.float32)
+
+
+def small_int(seed: int, shape, lo: int = -8, hi: int = 8) -> np.ndarray:
+    """float32 matrix of integers in [lo, hi] (top 32 bits modulo the range)."""
+    n = int(np.prod(shape, dtype=np.int64))
+    t = splitmix64(seed, n) >> np.uint64(32)
+    v = (t % np.uint64(hi - lo + 1)).astype(np.int64) + lo
+    return v.reshape(shape).astype(np.float32)
+
+
+def embed(x: np.ndarray, ld: int, fill: float = np.nan) -> np.ndarray:
+    """Place a rows x cols matrix in a row-major buffer with leading dimension
+    ``ld`` >= cols; the padding columns hold ``fill``. Returns the full
+    rows x ld buffer (the logical matrix is ``buf[:, :cols]``)."""
+    rows, cols = x.shape
+    if ld < cols:
+        raise ValueError("leading dimension smaller than the row length")
+    buf = np.full((rows, ld), fill, dtype=np.float32)
+    buf[:, :cols] = x
+    return buf
+
+
+# The five workloads: shape (M, N, K), value map, and what they stand for.
+WORKLOADS = {
+    "sq128": dict(M=128, N=128, K=128, dist="u01"),
+    "sq1024": dict(M=1024, N=1024, K=1024, dist="u01"),
+    "sq2048": dict(M=2048, N=2048, K=2048, dist="u01"),
+    "sq4096": dict(M=4096, N=4096, K=4096, dist="u01"),
+    "ragged": dict(M=3001, N=2047, K=4093, dist="pm1"),
+}
+
+
+def operands(M: int, N: int, K: int, dist: str = "u01",
+             seed_a: int = SEED_A, seed_b: int = SEED_B):
+    """Return (A, B) as contiguous float32 arrays of shape (M, K) and (K, N)."""
+    gen = {"u01": uniform01, "pm1": uniform_pm1, "int": small_int}[dist]
+    return gen(seed_a, (M, K)), gen(seed_b, (K, N))
