@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""FP32 SGEMM throughput on one MI355X: TFLOP/s at M = N = K = 4096 and the
+fraction of the chip's FP32 peak.
+
+One step is one call of the library's C ABI computing C = A * B for the
+4096^3 workload (row-major float32, A and B i.i.d. on [0, 1) from seeded
+SplitMix64), with A, B and C resident in HBM before timing starts. W untimed
+warm-up steps, then K steps timed with HIP events on the stream the kernel is
+launched on. Prints one JSON line on stdout; progress goes to stderr.
+
+Also reported:
+  roofline      the kernel's achieved TFLOP/s (2 M N K per launch over the
+                mean launch duration) against the FP32 matrix peak, and the
+                HBM traffic measured with rocprofv3 counters when it is on
+                file for the current kernel source;
+  cpu_baseline  the CPU oracle (double-accumulating triple loop, OpenMP) timed
+                on a bounded sample of the same product on the host cores;
+  ladder        every kernel variant timed on the same workload;
+  check         sampled elements compared with the oracle, and the
+                whole-matrix sum of C in double.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks.
+PEAK_FP32_TFLOPS = 157.3        # FP32 matrix cores (= packed-FP32 vector peak)
+PEAK_FP32_VALU_TFLOPS = 78.6    # scalar v_fma_f32: 256 CUs x 4 SIMD16 x 2 FLOP x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "FP32 SGEMM TFLOP/s at 4096^3 on 1 MI355X; % of FP32 peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mfma_sq4096_traffic.json")
+KERNEL_SOURCES = ["mfma.hip", "tile_io.hpp", "gemm.hpp"]
+
+
+def flops(M: int, N: int, K: int) -> int:
+    """Algorithmic FLOP of one product: K multiplies and K adds per element
+    of C ("Matrix Multiplication -- Naive to Tiled", section 03)."""
+    return 2 * M * N * K
+
+
+def compulsory_bytes(M: int, N: int, K: int) -> int:
+    """Bytes that must cross HBM at least once: read A and B, write C."""
+    return 4 * (M * K + K * N + M * N)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dense_fp32_matrix_sgemm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_per_launch():
+    """HBM bytes per launch from the committed counter runs, or None when they
+    are missing or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_launches(call, steps: int, warmup: int):
+    """Warm up, then time `steps` back-to-back launches with one HIP event
+    between consecutive launches on the launch stream. Returns (total ms,
+    list of per-launch ms)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    events[0].record(stream)
+    for i in range(steps):
+        call()
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [events[i].elapsed_time(events[i + 1]) for i in range(steps)]
+    return events[0].elapsed_time(events[steps]), per
+
+
+def cpu_baseline(A, B, target_s: float):
+    """The oracle on the first R rows of the product, R sized for about
+    target_s seconds of host time (at least 64 rows)."""
+    import numpy as np
+    import oracle
+    M, K = A.shape
+    N = B.shape[1]
+    probe = min(M, 64)
+    t0 = time.perf_counter()
+    oracle.gemm(np.ascontiguousarray(A[:probe]), B)
+    dt = time.perf_counter() - t0
+    rows = int(min(M, max(probe, probe * target_s / max(dt, 1e-6))))
+    rows = max(probe, rows - rows % 8) if rows < M else M
+    t0 = time.perf_counter()
+    oracle.gemm(np.ascontiguousarray(A[:rows]), B)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(flops(rows, N, K) / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product "
+                  f"({rows / M:.3f} of its work), {dt:.1f} s",
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--variant", default="best",
+                    choices=["best", "naive", "tiled", "regblock", "mfma"])
+    ap.add_argument("--size", type=int, default=4096, help="M = N = K")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ladder", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="host time budget of the CPU-baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the product, time a plain 256 MiB device copy "
+                         "(reference kernel for scaling the HBM byte counters)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("bench.py measures one GPU: this build has no multi-GPU path "
+               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})")
+        print(msg, file=sys.stderr)
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(json.dumps({"metric": METRIC, "error": msg, "n_gpus": args.gpus}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_fp32_matrix_sgemm_amd as sg
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    lib = sg.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 64 << 20  # floats: 256 MiB
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        total, per = time_launches(lambda: dst.copy_(src), args.steps, args.warmup)
+        ms = total / args.steps
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                          "ms_per_copy": round(ms, 5),
+                          "GB_per_s": round(8 * n / (ms / 1e3) / 1e9, 1)}))
+        return 0
+
+    M = N = K = args.size
+    log(f"generating {M}x{K} and {K}x{N} inputs")
+    A, B = synth.operands(M, N, K, "u01")
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.zeros((M, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    variant = sg.VARIANTS[args.variant]
+    resolved = sg.sgemm_best_variant(M, N, K) if variant == sg.SGEMM_BEST else variant
+    stream = torch.cuda.current_stream()
+    pa, pb, pc = dA.data_ptr(), dB.data_ptr(), dC.data_ptr()
+
+    def make_call(v):
+        def call():
+            rc = lib.sgemm(M, N, K, pa, K, pb, N, pc, N, stream.cuda_stream, v)
+            if rc != 0:
+                raise sg.SgemmError(rc)
+        return call
+
+    log(f"timing {args.steps} steps of variant {sg.sgemm_variant_name(resolved)} "
+        f"after {args.warmup} warm-up steps")
+    total_ms, per = time_launches(make_call(variant), args.steps, args.warmup)
+    ms = total_ms / args.steps
+    kernel_ms = sum(per) / len(per)
+    f = flops(M, N, K)
+    value = f / (ms / 1e3) / 1e12
+    achieved = f / (kernel_ms / 1e3) / 1e12
+    bound_peak = PEAK_FP32_TFLOPS if resolved == sg.SGEMM_MFMA else PEAK_FP32_VALU_TFLOPS
+    log(f"{ms:.4f} ms/step, {value:.2f} TFLOP/s ({100 * value / PEAK_FP32_TFLOPS:.1f}% of "
+        f"{PEAK_FP32_TFLOPS} peak)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "pct_of_fp32_peak": round(100 * value / PEAK_FP32_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"sgemm C=A*B, M=N=K={M}, row-major float32, A,B i.i.d. U[0,1) "
+                        "(SplitMix64 seeds 42/43), C overwritten",
+            "M": M, "N": N, "K": K,
+            "variant": sg.sgemm_variant_name(resolved),
+        },
+        "roofline": {
+            "bound": "mfma" if resolved == sg.SGEMM_MFMA else "alu",
+            "achieved": round(achieved, 3),
+            "peak": bound_peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / bound_peak, 4),
+            "traffic": traffic_per_launch() if (M == 4096 and resolved == sg.SGEMM_MFMA) else None,
+            "kernel_ms_mean": round(kernel_ms, 5),
+            "kernel_ms_min": round(min(per), 5),
+            "compulsory_bytes": compulsory_bytes(M, N, K),
+        },
+    }
+
+    if not args.no_check:
+        import oracle
+        from oracle.check import excess
+        torch.cuda.synchronize()
+        C = dC.cpu().numpy()
+        rng = np.random.default_rng(1)
+        rows = np.concatenate([[0, 0, M - 1, M - 1], rng.integers(0, M, 2044)])
+        cols = np.concatenate([[0, N - 1, 0, N - 1], rng.integers(0, N, 2044)])
+        ref, sabs = oracle.gemm_entries(A, B, rows, cols)
+        worst = float(excess(C[rows, cols], ref, sabs).max())
+        out["check"] = {
+            "sampled_elements": int(rows.size),
+            "worst_error_over_bound": round(worst, 4),
+            "pass": bool(worst <= 1.0),
+            "checksum_sum_C_double": float(C.astype(np.float64).sum()),
+        }
+        log(f"check: {rows.size} sampled elements, worst error {worst:.3f} of bound")
+
+    if not args.no_ladder:
+        ladder = {}
+        for name in ("naive", "tiled", "regblock", "mfma"):
+            code = sg.VARIANTS[name]
+            call = make_call(code)
+            call()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            call()
+            torch.cuda.synchronize()
+            one = time.perf_counter() - t0
+            reps = max(3, min(50, int(0.5 / max(one, 1e-6))))
+            tot, per_v = time_launches(call, reps, 1)
+            vms = tot / reps
+            tf = f / (vms / 1e3) / 1e12
+            ceiling = PEAK_FP32_TFLOPS if code == sg.SGEMM_MFMA else PEAK_FP32_VALU_TFLOPS
+            ladder[name] = {"ms": round(vms, 4), "TFLOP/s": round(tf, 3),
+                            "pct_of_fp32_peak": round(100 * tf / PEAK_FP32_TFLOPS, 2),
+                            "ceiling_TFLOP/s": ceiling,
+                            "frac_of_ceiling": round(tf / ceiling, 4), "reps": reps}
+            log(f"ladder {name}: {vms:.3f} ms, {tf:.2f} TFLOP/s")
+        out["ladder"] = ladder
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the product")
+        out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
+        log(f"cpu baseline: {out['cpu_baseline']}")
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,163 @@
+"""FP32 matrix multiply C = A * B on AMD MI355X (gfx950).
+
+Python binding of the C ABI declared in ``include/sgemm.h``: argument
+marshalling only. Every step of the product runs in the HIP kernels of
+``lib/libsgemm.so``; there is no CPU path. PyTorch supplies device buffers
+and streams.
+
+Raw entry points (same names and arguments as the C ABI):
+    sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream, variant) -> status
+    sgemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, variant) -> status
+    sgemm_status_string(status) -> str
+    sgemm_variant_name(variant) -> str | None
+    sgemm_best_variant(M, N, K) -> variant
+Pointers are integers (device addresses); ``stream`` is a hipStream_t as an
+integer (0 = null stream).
+
+Tensor convenience:
+    matmul(A, B, out=None, variant="best") -> C
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libsgemm.so")
+
+# Status codes (sgemm_status).
+SGEMM_OK = 0
+SGEMM_ERR_DIM = -1
+SGEMM_ERR_LD = -2
+SGEMM_ERR_NULL = -3
+SGEMM_ERR_VARIANT = -4
+SGEMM_ERR_LAUNCH = -5
+SGEMM_ERR_DEVICE = -6
+SGEMM_ERR_ALIAS = -7
+
+# Variant codes (sgemm_variant).
+SGEMM_BEST = -1
+SGEMM_NAIVE = 0
+SGEMM_TILED = 1
+SGEMM_REGBLOCK = 2
+SGEMM_MFMA = 3
+VARIANTS = {"best": SGEMM_BEST, "naive": SGEMM_NAIVE, "tiled": SGEMM_TILED,
+            "regblock": SGEMM_REGBLOCK, "mfma": SGEMM_MFMA}
+
+# Symbols the shared library exports (the functions of include/sgemm.h).
+EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_status_string",
+           "sgemm_variant_name", "sgemm_best_variant")
+
+_lib = None
+
+
+class SgemmError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"sgemm status {status}: {sgemm_status_string(status)}")
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libsgemm.so; raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(
+            f"{p} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(p)
+    i, vp = ctypes.c_int, ctypes.c_void_p
+    lib.sgemm.argtypes = [i, i, i, vp, i, vp, i, vp, i, vp, i]
+    lib.sgemm.restype = i
+    lib.sgemm_check_args.argtypes = [i, i, i, vp, i, vp, i, vp, i, i]
+    lib.sgemm_check_args.restype = i
+    lib.sgemm_status_string.argtypes = [i]
+    lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_variant_name.argtypes = [i]
+    lib.sgemm_variant_name.restype = ctypes.c_char_p
+    lib.sgemm_best_variant.argtypes = [i, i, i]
+    lib.sgemm_best_variant.restype = i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream, variant) -> int:
+    return load_library().sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream, variant)
+
+
+def sgemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, variant) -> int:
+    return load_library().sgemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, variant)
+
+
+def sgemm_status_string(status: int) -> str:
+    return load_library().sgemm_status_string(status).decode()
+
+
+def sgemm_variant_name(variant: int):
+    r = load_library().sgemm_variant_name(variant)
+    return None if r is None else r.decode()
+
+
+def sgemm_best_variant(M: int, N: int, K: int) -> int:
+    return load_library().sgemm_best_variant(M, N, K)
+
+
+def _variant_code(variant) -> int:
+    if isinstance(variant, str):
+        if variant not in VARIANTS:
+            raise ValueError(f"unknown variant {variant!r}; one of {sorted(VARIANTS)}")
+        return VARIANTS[variant]
+    return int(variant)
+
+
+def _ld(t) -> int:
+    """Leading dimension of a row-major 2-D tensor (rows one stride apart)."""
+    rows, cols = t.shape
+    if rows > 1:
+        return t.stride(0)
+    return max(cols, 1)
+
+
+def matmul(A, B, out=None, variant="best"):
+    """C = A @ B for float32 CUDA tensors A (M x K) and B (K x N).
+
+    Operands may be row-major views with a row stride larger than the row
+    length (sub-matrices); ``out`` (M x N, same rules) is overwritten. The
+    kernel is enqueued on the current stream of A's device.
+    """
+    import torch
+
+    for name, t in (("A", A), ("B", B)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise TypeError(f"{name} must be a 2-D torch.Tensor")
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} @ {tuple(B.shape)}")
+    if B.device != A.device:
+        raise ValueError("A and B are on different devices")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif (out.dtype != torch.float32 or out.device != A.device
+          or tuple(out.shape) != (M, N)):
+        raise ValueError("out must be a float32 M x N tensor on A's device")
+    for name, t in (("A", A), ("B", B), ("out", out)):
+        if t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must be row-major (unit column stride)")
+    with torch.cuda.device(A.device):
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+        rc = sgemm(M, N, K, A.data_ptr() or None, _ld(A), B.data_ptr() or None, _ld(B),
+                   out.data_ptr() or None, _ld(out), stream or None, _variant_code(variant))
+    if rc != SGEMM_OK:
+        raise SgemmError(rc)
+    return out

@@ -1,0 +1,81 @@
+// Host-side argument checks, status strings and variant names of the C ABI.
+//
+// Pure C++: no HIP header and no device call, so these entry points work
+// (and are tested, also under the host sanitizers) on a machine without a GPU.
+#include <cstdint>
+
+#include "sgemm.h"
+
+namespace {
+
+// Byte range [lo, hi) spanned by a rows x cols row-major matrix with leading
+// dimension ld (elements); empty when rows or cols is 0.
+struct Span {
+    std::uintptr_t lo, hi;
+};
+
+Span span_of(const float *p, int rows, int cols, int ld)
+{
+    const std::uintptr_t base = reinterpret_cast<std::uintptr_t>(p);
+    if (rows <= 0 || cols <= 0) return {base, base};
+    const std::uint64_t last = static_cast<std::uint64_t>(rows - 1) * static_cast<std::uint64_t>(ld) +
+                               static_cast<std::uint64_t>(cols);
+    return {base, base + last * sizeof(float)};
+}
+
+bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool known_variant(int v) { return v >= SGEMM_BEST && v <= SGEMM_MFMA; }
+
+}  // namespace
+
+extern "C" int sgemm_check_args(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                                const float *C, int ldc, int variant)
+{
+    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return SGEMM_ERR_LD;
+    if (!known_variant(variant)) return SGEMM_ERR_VARIANT;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (C == nullptr) return SGEMM_ERR_NULL;
+    if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_ERR_NULL;
+    if (K > 0) {
+        const Span c = span_of(C, M, N, ldc);
+        if (overlap(c, span_of(A, M, K, lda)) || overlap(c, span_of(B, K, N, ldb))) return SGEMM_ERR_ALIAS;
+    }
+    return SGEMM_OK;
+}
+
+extern "C" const char *sgemm_status_string(int status)
+{
+    switch (status) {
+    case SGEMM_OK: return "success";
+    case SGEMM_ERR_DIM: return "negative matrix dimension";
+    case SGEMM_ERR_LD: return "leading dimension smaller than the row length";
+    case SGEMM_ERR_NULL: return "NULL matrix pointer with a non-empty extent";
+    case SGEMM_ERR_VARIANT: return "unknown kernel variant";
+    case SGEMM_ERR_LAUNCH: return "kernel launch failed";
+    case SGEMM_ERR_DEVICE: return "no usable gfx950 HIP device";
+    case SGEMM_ERR_ALIAS: return "C overlaps A or B";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char *sgemm_variant_name(int variant)
+{
+    switch (variant) {
+    case SGEMM_BEST: return "best";
+    case SGEMM_NAIVE: return "naive";
+    case SGEMM_TILED: return "tiled";
+    case SGEMM_REGBLOCK: return "regblock";
+    case SGEMM_MFMA: return "mfma";
+    default: return nullptr;
+    }
+}
+
+extern "C" int sgemm_best_variant(int M, int N, int K)
+{
+    (void)M;
+    (void)N;
+    (void)K;
+    return SGEMM_MFMA;
+}

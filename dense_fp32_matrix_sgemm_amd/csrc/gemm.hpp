@@ -1,0 +1,72 @@
+// Internal interface between the C ABI's dispatcher and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sgemm_impl {
+
+// One product C = A * B, row-major, leading dimensions in elements. Offsets
+// are formed in 64 bits so that any int-sized problem indexes correctly.
+struct Problem {
+    const float *A;
+    const float *B;
+    float *C;
+    std::int64_t lda, ldb, ldc;
+    int M, N, K;
+};
+
+// Each launcher enqueues the variant's kernel(s) on `stream` and returns the
+// launch status; the problem has already been validated and is non-empty
+// (M > 0, N > 0; K may be 0, in which case the kernels store zeros).
+hipError_t launch_naive(const Problem &p, hipStream_t stream);
+hipError_t launch_tiled(const Problem &p, hipStream_t stream);
+hipError_t launch_regblock(const Problem &p, hipStream_t stream);
+hipError_t launch_mfma(const Problem &p, hipStream_t stream);
+
+// Largest grid extent used along y (row blocks); kernels loop over the rest.
+constexpr unsigned kMaxGridY = 65535;
+
+// Splits a product over a 1-D grid of BM x BN tiles into bands of at most
+// 2^22 tiles each (far inside the grid limit) and calls launch(sub, tiles_m,
+// tiles_n) for each band. A band is itself a product: A and C start at its
+// first row, B and C at its first column. Band edges fall on multiples of BM
+// and BN, so 16-byte alignment of the operands carries over.
+template <int BM, int BN, class Launch>
+hipError_t for_each_band(const Problem &p, Launch &&launch)
+{
+    constexpr std::int64_t kMaxTiles = std::int64_t(1) << 22;
+    const std::int64_t tiles_n_all = (std::int64_t(p.N) + BN - 1) / BN;
+    const std::int64_t band_tn = tiles_n_all < kMaxTiles ? tiles_n_all : kMaxTiles;
+    const std::int64_t band_tm = kMaxTiles / band_tn;
+    for (std::int64_t r0 = 0; r0 < p.M; r0 += band_tm * BM) {
+        for (std::int64_t c0 = 0; c0 < p.N; c0 += band_tn * BN) {
+            Problem q = p;
+            q.M = int(p.M - r0 < band_tm * BM ? p.M - r0 : band_tm * BM);
+            q.N = int(p.N - c0 < band_tn * BN ? p.N - c0 : band_tn * BN);
+            if (p.K > 0) {  // A and B are not read (and may be NULL) when K == 0
+                q.A = p.A + r0 * p.lda;
+                q.B = p.B + c0;
+            }
+            q.C = p.C + r0 * p.ldc + c0;
+            const int tiles_m = int((q.M + BM - 1) / BM), tiles_n = int((q.N + BN - 1) / BN);
+            const hipError_t e = launch(q, tiles_m, tiles_n);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+inline bool aligned16(const void *ptr) { return (reinterpret_cast<std::uintptr_t>(ptr) & 15u) == 0; }
+
+// True when every row of A, B and C starts on a 16-byte boundary, so 4-wide
+// chunks at column offsets that are multiples of 4 can move as one 128-bit
+// access.
+inline bool rows_aligned16(const Problem &p)
+{
+    return aligned16(p.A) && aligned16(p.B) && aligned16(p.C) && p.lda % 4 == 0 && p.ldb % 4 == 0 &&
+           p.ldc % 4 == 0;
+}
+
+}  // namespace sgemm_impl

@@ -1,0 +1,85 @@
+// Device helpers shared by the LDS-staged kernels: guarded 4-wide loads and
+// stores, and the mapping from work-group number to output tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sgemm_impl {
+
+// Four consecutive elements (row, c .. c+3) of a row-major rows x cols matrix
+// with leading dimension ld; elements outside the matrix read as 0 (the
+// zero-padding that makes ragged tiles correct: "Matrix Multiplication --
+// Naive to Tiled", section 05; "Shared Memory Tiling for Matrix
+// Multiplication", traps). `inside` is the caller's promise that the whole
+// chunk lies in the matrix. With VEC the chunk is then read with one 16-byte
+// load; the caller guarantees 16-byte alignment (base aligned, ld and c
+// multiples of 4).
+template <bool VEC>
+__device__ __forceinline__ float4 load4(const float *base, std::int64_t ld, std::int64_t row, int c,
+                                        std::int64_t rows, int cols, bool inside)
+{
+    const float *p = base + row * ld + c;
+    if (inside) {
+        if constexpr (VEC) {
+            return *reinterpret_cast<const float4 *>(p);
+        } else {
+            return make_float4(p[0], p[1], p[2], p[3]);
+        }
+    }
+    const bool r = row < rows;
+    float4 v;
+    v.x = (r && c + 0 < cols) ? p[0] : 0.0f;
+    v.y = (r && c + 1 < cols) ? p[1] : 0.0f;
+    v.z = (r && c + 2 < cols) ? p[2] : 0.0f;
+    v.w = (r && c + 3 < cols) ? p[3] : 0.0f;
+    return v;
+}
+
+// Store n (1..4) consecutive floats v[0..n-1] at (row, c ..) of C, dropping
+// elements outside rows x cols. With VEC and all four inside, one 16-byte
+// store (same alignment contract as load4).
+template <bool VEC>
+__device__ __forceinline__ void store4(float *base, std::int64_t ld, std::int64_t row, int c, std::int64_t rows,
+                                       int cols, float4 v)
+{
+    if (row >= rows) return;
+    float *p = base + row * ld + c;
+    if (VEC && c + 3 < cols) {
+        *reinterpret_cast<float4 *>(p) = v;
+        return;
+    }
+    if (c + 0 < cols) p[0] = v.x;
+    if (c + 1 < cols) p[1] = v.y;
+    if (c + 2 < cols) p[2] = v.z;
+    if (c + 3 < cols) p[3] = v.w;
+}
+
+// Work-group number -> output tile (tm, tn).
+//
+// The dispatcher hands consecutive work-group numbers to the eight XCDs in
+// turn (number w runs on XCD w % 8), and each XCD has its own L2. The first
+// step renumbers so that each XCD receives one contiguous run of logical
+// tiles; the second walks the logical tiles in bands of `group_m` tile rows,
+// column by column inside a band, so that the tiles resident on one XCD at a
+// time share a few row panels of A and column panels of B in its L2.
+// Both steps are bijections on [0, tiles_m * tiles_n).
+__device__ __forceinline__ void tile_of_workgroup(unsigned w, unsigned n_wg, int tiles_m, int group_m, int &tm,
+                                                  int &tn)
+{
+    constexpr unsigned kXcds = 8;
+    const unsigned q = n_wg / kXcds, r = n_wg % kXcds;
+    const unsigned xcd = w % kXcds, idx = w / kXcds;
+    const unsigned logical = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+
+    const unsigned tiles_n = n_wg / unsigned(tiles_m);
+    const unsigned band = unsigned(group_m) * tiles_n;
+    const unsigned first_m = (logical / band) * unsigned(group_m);
+    const unsigned rows_in_band = min(unsigned(tiles_m) - first_m, unsigned(group_m));
+    const unsigned in_band = logical % band;
+    tm = int(first_m + in_band % rows_in_band);
+    tn = int(in_band / rows_in_band);
+}
+
+}  // namespace sgemm_impl

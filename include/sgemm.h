@@ -1,0 +1,126 @@
+/*
+ * sgemm.h -- C ABI of the MI355X (gfx950) FP32 matrix multiply.
+ *
+ * Operation ("Shared Memory Tiling for Matrix Multiplication", opening
+ * definition; "Matrix Multiplication -- Naive to Tiled", section 02):
+ *
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j],   0 <= i < M, 0 <= j < N
+ *
+ * A is M x K, B is K x N, C is M x N, all float32 and row-major: element
+ * (r, c) of a matrix with leading dimension ld lives at ptr[r * ld + c]
+ * ("Matrix Multiplication -- Naive to Tiled", section 02 indexes A[row*K+i],
+ * B[i*N+col], C[row*N+col]; leading dimensions generalise the row length as
+ * the BLAS call of section 07 does). C is overwritten: its old contents are
+ * never read (section 07's vendor call with alpha = 1, beta = 0; every kernel
+ * on the pages stores with '='). Elements of C's rows beyond column N-1 (the
+ * padding up to ldc) are never touched.
+ *
+ * Products are formed and summed in float32 (fused multiply-add, round to
+ * nearest even). The summation order is the kernel's own; the result is within
+ * 1e-5 * sum_k |A[i][k]| * |B[k][j]| + 1e-6 of the exact sum, and exact when
+ * every partial sum is an integer below 2^24 (small-integer inputs).
+ *
+ * All matrix pointers are DEVICE pointers on the calling thread's current HIP
+ * device. The caller owns every buffer; the library allocates nothing per
+ * call, keeps no pointer after returning and has no mutable global state
+ * besides a per-device cache of the device's architecture, so calls from
+ * several host threads are safe.
+ */
+#ifndef SGEMM_H
+#define SGEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. Every entry point returns one; none ever exits the process
+ * (unlike the pages' error macro, which prints and calls exit()). */
+typedef enum sgemm_status {
+    SGEMM_OK = 0,
+    SGEMM_ERR_DIM = -1,      /* M, N or K negative                              */
+    SGEMM_ERR_LD = -2,       /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+    SGEMM_ERR_NULL = -3,     /* NULL matrix pointer with a non-empty extent      */
+    SGEMM_ERR_VARIANT = -4,  /* unknown variant code                             */
+    SGEMM_ERR_LAUNCH = -5,   /* the HIP launch itself failed (hipGetLastError)   */
+    SGEMM_ERR_DEVICE = -6,   /* no usable HIP device, or it is not gfx950        */
+    SGEMM_ERR_ALIAS = -7     /* C's extent overlaps A's or B's                   */
+} sgemm_status;
+
+/* Kernel variants: the ladder from the pages' naive kernel to matrix cores.
+ *  NAIVE    one work-item per element of C, operands straight from global
+ *           memory ("Matrix Multiplication -- Naive to Tiled", section 02).
+ *  TILED    16 x 16 tiles of A and B staged in LDS, zero-filled at the edges,
+ *           two barriers per K step (same page, sections 04-05).
+ *  REGBLOCK 128 x 128 LDS tiles, an 8 x 8 block of C per work-item in
+ *           registers, 128-bit global loads, double-buffered LDS (same page,
+ *           section 07; "From 306 ms to 86 ms", "Register blocking").
+ *  MFMA     the same tiling fed to the CDNA matrix cores with
+ *           v_mfma_f32_32x32x2_f32 (FP32 in, FP32 accumulate).
+ *  BEST     whichever variant is fastest for the shape (currently MFMA). */
+typedef enum sgemm_variant {
+    SGEMM_BEST = -1,
+    SGEMM_NAIVE = 0,
+    SGEMM_TILED = 1,
+    SGEMM_REGBLOCK = 2,
+    SGEMM_MFMA = 3
+} sgemm_variant;
+
+/*
+ * C = A * B on `stream` (a hipStream_t of the current device; NULL means the
+ * null stream).
+ *
+ * Arguments
+ *   M, N, K        sizes; each >= 0.
+ *   A, lda         M x K operand, lda >= max(1, K).
+ *   B, ldb         K x N operand, ldb >= max(1, N).
+ *   C, ldc         M x N result, ldc >= max(1, N); overwritten.
+ *   stream         queue to launch on; the call returns without waiting.
+ *   variant        an sgemm_variant code.
+ *
+ * Behaviour
+ *   - Arguments are checked on the host, in this order, before any HIP call:
+ *     sizes, leading dimensions, variant, then (only if M > 0 and N > 0)
+ *     NULL pointers and overlap of C with A or B.
+ *   - M == 0 or N == 0: nothing to do; returns SGEMM_OK without touching the
+ *     GPU (pointers may then be NULL).
+ *   - K == 0: the sum is empty, so the M x N window of C is set to 0
+ *     (A and B are not read and may be NULL).
+ *   - Otherwise one kernel is enqueued. Errors a kernel meets while running
+ *     (a fault from a bad pointer, say) are not seen here; they surface at the
+ *     caller's next synchronisation, as for any asynchronous HIP launch.
+ *   - C must not overlap A or B (checked: SGEMM_ERR_ALIAS).
+ *
+ * Returns SGEMM_OK or a negative sgemm_status.
+ */
+int sgemm(int M, int N, int K,
+          const float *A, int lda,
+          const float *B, int ldb,
+          float *C, int ldc,
+          void *stream, int variant);
+
+/*
+ * The host-side argument checks of sgemm() alone, with the same codes and in
+ * the same order; makes no HIP call and touches no memory. Returns SGEMM_OK
+ * when sgemm() would go on to launch (or return early for an empty C).
+ */
+int sgemm_check_args(int M, int N, int K,
+                     const float *A, int lda,
+                     const float *B, int ldb,
+                     const float *C, int ldc,
+                     int variant);
+
+/* Static English text for a status code ("unknown status" otherwise). */
+const char *sgemm_status_string(int status);
+
+/* Static name of a variant code ("naive", "tiled", "regblock", "mfma",
+ * "best"), or NULL for an unknown code. */
+const char *sgemm_variant_name(int variant);
+
+/* The concrete variant SGEMM_BEST resolves to for an M x N x K product. */
+int sgemm_best_variant(int M, int N, int K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_H */

@@ -1,0 +1,54 @@
+"""Helpers for the GPU tests: place host matrices in device buffers (optionally
+with a larger leading dimension and a misaligning start offset), call the C ABI
+through the binding, and read the result back."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import dense_fp32_matrix_sgemm_amd as sg
+
+SENTINEL = -12345.0
+
+
+def device_matrix(x: np.ndarray, ld: int | None = None, offset: int = 0,
+                  fill: float = float("nan")):
+    """A rows x cols device view of ``x`` with leading dimension ``ld`` that
+    starts ``offset`` floats into a buffer whose other elements hold ``fill``.
+    Returns (view, backing buffer)."""
+    rows, cols = x.shape
+    ld = max(cols, 1) if ld is None else ld
+    buf = torch.full((offset + rows * ld + 8,), fill, dtype=torch.float32)
+    view = torch.as_strided(buf, (rows, cols), (ld, 1), offset)
+    view.copy_(torch.from_numpy(np.ascontiguousarray(x)))
+    dbuf = buf.cuda()
+    return torch.as_strided(dbuf, (rows, cols), (ld, 1), offset), dbuf
+
+
+def gemm(A: np.ndarray, B: np.ndarray, variant, ld_pad=(0, 0, 0), offset=(0, 0, 0),
+         stream=None, return_buffer=False):
+    """Run the library on copies of A and B; returns C (numpy float32).
+
+    C's buffer starts filled with SENTINEL; with ``return_buffer`` the whole
+    backing buffer of C and its (ld, offset) are returned too, so a test can
+    check that nothing outside the M x N window was written.
+    """
+    M, K = A.shape
+    N = B.shape[1]
+    dA, _ = device_matrix(A, K + ld_pad[0], offset[0])
+    dB, _ = device_matrix(B, N + ld_pad[1], offset[1])
+    ldc = N + ld_pad[2]
+    dC, cbuf = device_matrix(np.full((M, N), SENTINEL, np.float32), ldc, offset[2],
+                             fill=SENTINEL)
+    s = stream or torch.cuda.current_stream()
+    rc = sg.sgemm(M, N, K, dA.data_ptr(), max(K + ld_pad[0], 1), dB.data_ptr(),
+                  max(N + ld_pad[1], 1), dC.data_ptr(), max(ldc, 1), s.cuda_stream,
+                  sg.VARIANTS[variant] if isinstance(variant, str) else variant)
+    if rc != sg.SGEMM_OK:
+        raise sg.SgemmError(rc)
+    s.synchronize()
+    C = dC.cpu().numpy()
+    if return_buffer:
+        return C, cbuf.cpu().numpy(), max(ldc, 1), offset[2]
+    return C

@@ -1,0 +1,121 @@
+"""The C ABI library on the host: it loads, exports what include/sgemm.h
+declares, and rejects bad arguments before any GPU call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_fp32_matrix_sgemm_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+
+A, B, C = 0x10000, 0x20000000, 0x40000000  # distinct fake addresses, never touched
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgemm\w*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sg.load_library()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_functions() == sorted(sg.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    codes = [sg.SGEMM_OK, sg.SGEMM_ERR_DIM, sg.SGEMM_ERR_LD, sg.SGEMM_ERR_NULL,
+             sg.SGEMM_ERR_VARIANT, sg.SGEMM_ERR_LAUNCH, sg.SGEMM_ERR_DEVICE, sg.SGEMM_ERR_ALIAS]
+    texts = [sg.sgemm_status_string(c) for c in codes]
+    assert len(set(texts)) == len(texts)
+    assert "unknown status" not in texts
+    assert sg.sgemm_status_string(12345) == "unknown status"
+
+
+def test_variant_names(lib):
+    for name, code in sg.VARIANTS.items():
+        assert sg.sgemm_variant_name(code) == name
+    assert sg.sgemm_variant_name(4) is None
+    assert sg.sgemm_variant_name(-2) is None
+    assert sg.sgemm_best_variant(4096, 4096, 4096) in (0, 1, 2, 3)
+
+
+CASES = [
+    # (M, N, K, A, lda, B, ldb, C, ldc, variant) -> status
+    ((-1, 4, 4, A, 4, B, 4, C, 4, 0), sg.SGEMM_ERR_DIM),
+    ((4, -1, 4, A, 4, B, 4, C, 4, 0), sg.SGEMM_ERR_DIM),
+    ((4, 4, -1, A, 4, B, 4, C, 4, 0), sg.SGEMM_ERR_DIM),
+    ((4, 4, 4, A, 3, B, 4, C, 4, 0), sg.SGEMM_ERR_LD),
+    ((4, 4, 4, A, 4, B, 3, C, 4, 0), sg.SGEMM_ERR_LD),
+    ((4, 4, 4, A, 4, B, 4, C, 3, 0), sg.SGEMM_ERR_LD),
+    ((4, 4, 0, A, 0, B, 4, C, 4, 0), sg.SGEMM_ERR_LD),      # lda >= max(1, K)
+    ((0, 0, 0, None, 1, None, 1, None, 1, 0), sg.SGEMM_OK),  # empty, NULLs fine
+    ((4, 4, 4, A, 4, B, 4, C, 4, 4), sg.SGEMM_ERR_VARIANT),
+    ((4, 4, 4, A, 4, B, 4, C, 4, -2), sg.SGEMM_ERR_VARIANT),
+    ((0, 4, 4, A, 4, B, 4, C, 4, 7), sg.SGEMM_ERR_VARIANT),  # variant checked first
+    ((0, 4, 4, None, 4, None, 4, None, 4, 3), sg.SGEMM_OK),  # M == 0
+    ((4, 0, 4, None, 4, None, 1, None, 1, 3), sg.SGEMM_OK),  # N == 0
+    ((4, 4, 4, None, 4, B, 4, C, 4, 0), sg.SGEMM_ERR_NULL),
+    ((4, 4, 4, A, 4, None, 4, C, 4, 0), sg.SGEMM_ERR_NULL),
+    ((4, 4, 4, A, 4, B, 4, None, 4, 0), sg.SGEMM_ERR_NULL),
+    ((4, 4, 0, None, 1, None, 4, C, 4, 0), sg.SGEMM_OK),     # K == 0: A, B unused
+    ((4, 4, 0, None, 1, None, 4, None, 4, 0), sg.SGEMM_ERR_NULL),
+    # C overlapping A or B
+    ((4, 4, 4, A, 4, B, 4, A + 4 * 15, 4, 0), sg.SGEMM_ERR_ALIAS),   # C starts in A's last element
+    ((4, 4, 4, A, 4, B, 4, A + 4 * 16, 4, 0), sg.SGEMM_OK),          # C starts right after A
+    ((4, 4, 4, A, 4, B, 4, B - 4 * 16, 4, 0), sg.SGEMM_OK),          # C ends right before B
+    ((4, 4, 4, A, 4, B, 4, B - 4 * 15, 4, 0), sg.SGEMM_ERR_ALIAS),
+    ((4, 4, 0, A, 1, B, 4, A, 4, 0), sg.SGEMM_OK),                   # K == 0: A not read
+    # Large, overflow-prone extents are handled in 64 bits
+    ((2**31 - 1, 2, 2, A, 2, B, 2, C, 2**31 - 1, 0), sg.SGEMM_ERR_ALIAS),
+]
+
+
+@pytest.mark.parametrize("args,want", CASES)
+def test_check_args(lib, args, want):
+    assert sg.sgemm_check_args(*args) == want
+
+
+@pytest.mark.parametrize("args,want", [c for c in CASES if c[1] != sg.SGEMM_OK])
+def test_sgemm_rejects_before_touching_the_gpu(lib, args, want):
+    M, N, K, pa, lda, pb, ldb, pc, ldc, variant = args
+    assert sg.sgemm(M, N, K, pa, lda, pb, ldb, pc, ldc, None, variant) == want
+
+
+def test_empty_product_returns_ok_without_gpu(lib):
+    assert sg.sgemm(0, 5, 5, None, 5, None, 5, None, 5, None, 3) == sg.SGEMM_OK
+    assert sg.sgemm(5, 0, 5, None, 5, None, 1, None, 1, None, 3) == sg.SGEMM_OK
+
+
+def test_no_device_is_reported_not_crashed(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    rc = sg.sgemm(4, 4, 4, A, 4, B, 4, C, 4, None, 0)
+    assert rc == sg.SGEMM_ERR_DEVICE
+
+
+def test_matmul_rejects_bad_tensors():
+    import torch
+    a = torch.zeros(3, 4)
+    with pytest.raises(ValueError):
+        sg.matmul(a, torch.zeros(4, 2))          # CPU tensors: no CPU path
+    with pytest.raises(TypeError):
+        sg.matmul(a.double(), torch.zeros(4, 2))
+    with pytest.raises(TypeError):
+        sg.matmul(torch.zeros(3), torch.zeros(3, 2))
+    with pytest.raises(ValueError):
+        sg._variant_code("nope")
