@@ -32,6 +32,8 @@
 //
 // Ragged shapes: tiles and slabs that cross the edge of A, B or C load zeros
 // outside and drop stores outside; interior tiles take the unguarded path.
+#include <type_traits>
+
 #include "gemm.hpp"
 #include "tile_io.hpp"
 
@@ -39,6 +41,9 @@ namespace sgemm_impl {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+// Native 4-wide vector: copies of it stay in registers (copies of the HIP
+// float4 struct through pointers become memcpy and can end up in scratch).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int N>
 struct Vec;
@@ -72,7 +77,13 @@ struct MfmaConfig {
     static constexpr int kPitchA = BK + kPadA;
     static constexpr int kChunksA = BM * BK / 4 / kThreads;  // 4-wide chunks per work-item
     static constexpr int kChunksB = BK * BN / 4 / kThreads;
-    static constexpr int kGroupM = 8;
+#ifndef SGEMM_MFMA_GROUP_M
+#define SGEMM_MFMA_GROUP_M 8
+#endif
+    static constexpr int kGroupM = SGEMM_MFMA_GROUP_M;
+    // Waves per SIMD the register allocation aims at: one when a wave's
+    // accumulators alone fill the 256 AGPRs, two otherwise.
+    static constexpr int kWavesPerEU = MI * NJ * TI * 16 >= 256 ? 1 : 2;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(TI == 1 || TI == 2 || TI == 4, "column interleave must be 1, 2 or 4");
     static_assert(WN == 32 * TI * NJ, "wave tile width must split into interleaved groups");
@@ -88,6 +99,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tile
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
     constexpr int MI = Cfg::MI, NJ = Cfg::NJ, TI = Cfg::TI;
     constexpr int PA = Cfg::kPitchA;
+    constexpr int G = BK / 8;  // groups of 8 k per slab
     using VecB = typename Vec<TI>::T;
 
     __shared__ __attribute__((aligned(16))) float As[2][BM * PA];
@@ -105,9 +117,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tile
     const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
     const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
 
-    const bool rows_in = m0 + BM <= p.M;
-    const bool cols_in = n0 + BN <= p.N;
+    // Interior tiles run the pipelined loop over their whole slabs with
+    // unguarded loads and finish a partial last slab separately; edge tiles
+    // run the same loop with guarded loads throughout. The two loops are
+    // separate instantiations, so the guarded path's addresses are never
+    // live in the fast one.
+    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
     const int n_slabs = (p.K + BK - 1) / BK;
+    const int n_full = p.K / BK;
 
     floatx16 acc[MI][NJ][TI];
 #pragma unroll
@@ -117,83 +134,135 @@ __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tile
 #pragma unroll
             for (int t = 0; t < TI; ++t) acc[mi][nj][t] = floatx16{};
 
+    // Global -> register staging of one slab: chunk c of the A tile is row
+    // c / (BK/4), columns 4 (c % (BK/4)) ..; chunk c of the B tile is row
+    // c / (BN/4), columns 4 (c % (BN/4)) ...
     float4 ra[Cfg::kChunksA], rb[Cfg::kChunksB];
-
-    auto fetch = [&](int slab) {
+    auto fetch = [&](int slab, auto guarded) {
         const int k0 = slab * BK;
-        const bool k_in = k0 + BK <= p.K;
 #pragma unroll
         for (int q = 0; q < Cfg::kChunksA; ++q) {
             const int c = tid + q * Cfg::kThreads;
-            const int row = c / (BK / 4), kk = (c % (BK / 4)) * 4;
-            ra[q] = load4<VEC>(p.A, p.lda, m0 + row, k0 + kk, p.M, p.K, rows_in && k_in);
+            const std::int64_t row = m0 + c / (BK / 4);
+            const int col = k0 + (c % (BK / 4)) * 4;
+            if constexpr (decltype(guarded)::value)
+                ra[q] = load4_clamped(p.A, p.lda, row, col, p.M, p.K);
+            else
+                ra[q] = load4_inside<VEC>(p.A, p.lda, row, col);
         }
 #pragma unroll
         for (int q = 0; q < Cfg::kChunksB; ++q) {
             const int c = tid + q * Cfg::kThreads;
-            const int kr = c / (BN / 4), col = (c % (BN / 4)) * 4;
-            rb[q] = load4<VEC>(p.B, p.ldb, k0 + kr, n0 + col, p.K, p.N, k_in && cols_in);
+            const std::int64_t row = k0 + c / (BN / 4);
+            const int col = n0 + (c % (BN / 4)) * 4;
+            if constexpr (decltype(guarded)::value)
+                rb[q] = load4_clamped(p.B, p.ldb, row, col, p.K, p.N);
+            else
+                rb[q] = load4_inside<VEC>(p.B, p.ldb, row, col);
         }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, int slab, auto guarded) {
+        if constexpr (decltype(guarded)::value) {
+            const int k0 = slab * BK;
+#pragma unroll
+            for (int q = 0; q < Cfg::kChunksA; ++q) {
+                const int c = tid + q * Cfg::kThreads;
+                zero_outside(ra[q], m0 + c / (BK / 4), k0 + (c % (BK / 4)) * 4, p.M, p.K);
+            }
+#pragma unroll
+            for (int q = 0; q < Cfg::kChunksB; ++q) {
+                const int c = tid + q * Cfg::kThreads;
+                zero_outside(rb[q], k0 + c / (BN / 4), n0 + (c % (BN / 4)) * 4, p.K, p.N);
+            }
+        }
 #pragma unroll
         for (int q = 0; q < Cfg::kChunksA; ++q) {
             const int c = tid + q * Cfg::kThreads;
-            const int row = c / (BK / 4), kk = (c % (BK / 4)) * 4;
-            *reinterpret_cast<float4 *>(&As[buf][row * PA + kk]) = ra[q];
+            *reinterpret_cast<float4 *>(&As[buf][(c / (BK / 4)) * PA + (c % (BK / 4)) * 4]) = ra[q];
         }
 #pragma unroll
         for (int q = 0; q < Cfg::kChunksB; ++q) {
             const int c = tid + q * Cfg::kThreads;
-            const int kr = c / (BN / 4), col = (c % (BN / 4)) * 4;
-            *reinterpret_cast<float4 *>(&Bs[buf][kr * BN + col]) = rb[q];
+            *reinterpret_cast<float4 *>(&Bs[buf][(c / (BN / 4)) * BN + (c % (BN / 4)) * 4]) = rb[q];
         }
     };
-    auto multiply = [&](int buf) {
+
+    // Operand fragments of one group of 8 k, double-buffered in registers so
+    // the reads of group g+1 are in flight while group g's MFMAs issue.
+    float4 af[2][MI];
+    VecB bf[2][4][NJ];
+    auto read_frags = [&](int buf, int g, int slot) {
         const float *as = As[buf];
         const float *bs = Bs[buf];
 #pragma unroll
-        for (int g = 0; g < BK / 8; ++g) {
-            float4 af[MI];
-            VecB bf[4][NJ];
+        for (int mi = 0; mi < MI; ++mi)
+            af[slot][mi] = *reinterpret_cast<const float4 *>(&as[(wm0 + mi * 32 + l32) * PA + 8 * g + 4 * h]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int nj = 0; nj < NJ; ++nj)
+                bf[slot][s][nj] =
+                    *reinterpret_cast<const VecB *>(&bs[(8 * g + 4 * h + s) * BN + wn0 + nj * 32 * TI + l32 * TI]);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
-                af[mi] = *reinterpret_cast<const float4 *>(&as[(wm0 + mi * 32 + l32) * PA + 8 * g + 4 * h]);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int nj = 0; nj < NJ; ++nj)
-                    bf[s][nj] = *reinterpret_cast<const VecB *>(
-                        &bs[(8 * g + 4 * h + s) * BN + wn0 + nj * 32 * TI + l32 * TI]);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+                    for (int t = 0; t < TI; ++t)
+                        acc[mi][nj][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            elem(af[slot][mi], s), elem(bf[slot][s][nj], t), acc[mi][nj][t], 0, 0, 0);
+    };
+    // Multiply out one LDS buffer; `between` runs half-way through.
+    auto multiply = [&](int buf, auto &&between) {
+        read_frags(buf, 0, 0);
 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                    for (int nj = 0; nj < NJ; ++nj)
-#pragma unroll
-                        for (int t = 0; t < TI; ++t)
-                            acc[mi][nj][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                elem(af[mi], s), elem(bf[s][nj], t), acc[mi][nj][t], 0, 0, 0);
+        for (int g = 0; g < G; ++g) {
+            if (g + 1 < G) read_frags(buf, g + 1, (g + 1) & 1);
+            if (g == G / 2) between();
+            mfmas(g & 1);
         }
     };
 
-    if (n_slabs > 0) {
-        fetch(0);
-        stash(0);
+    // Slabs [0, n) with the two-buffer pipeline: slab t+1 waits in registers
+    // while slab t is multiplied; half-way through slab t it is written to the
+    // other LDS buffer (which every wave finished reading before the previous
+    // barrier) and the fetch of slab t+2 starts.
+    auto pipeline = [&](int n, auto guarded) {
+        if (n <= 0) return;
+        fetch(0, guarded);
+        stash(0, 0, guarded);
+        if (n > 1) fetch(1, guarded);
         __syncthreads();
-        for (int t = 0; t < n_slabs; ++t) {
+        for (int t = 0; t < n; ++t) {
             const int cur = t & 1;
-            const bool more = t + 1 < n_slabs;
-            if (more) fetch(t + 1);
-            multiply(cur);
-            if (more) stash(cur ^ 1);
+            multiply(cur, [&] {
+                if (t + 1 < n) {
+                    stash(cur ^ 1, t + 1, guarded);
+                    if (t + 2 < n) fetch(t + 2, guarded);
+                }
+            });
             __syncthreads();
         }
+    };
+
+    if (interior) {
+        pipeline(n_full, std::false_type{});
+        if (n_full < n_slabs) {  // partial last slab
+            fetch(n_full, std::true_type{});
+            stash(0, n_full, std::true_type{});
+            __syncthreads();
+            multiply(0, [] {});
+        }
+    } else {
+        pipeline(n_slabs, std::true_type{});
     }
 
     // Epilogue: register r of block (mi, nj, t) is row 8(r/4) + 4h + r%4 of
-    // the block and column TI*l32 + t of the column group.
+    // the block and column TI*l32 + t of its column group.
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -202,25 +271,184 @@ __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tile
             for (int r = 0; r < 16; ++r) {
                 const std::int64_t row = m0 + wm0 + mi * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                 const int col = n0 + wn0 + nj * 32 * TI + l32 * TI;
-                float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                float v[TI];
 #pragma unroll
                 for (int t = 0; t < TI; ++t) v[t] = acc[mi][nj][t][r];
-                if constexpr (TI == 4) {
-                    store4<VEC>(p.C, p.ldc, row, col, p.M, p.N, make_float4(v[0], v[1], v[2], v[3]));
-                } else {
-                    if (row < p.M) {
-#pragma unroll
-                        for (int t = 0; t < TI; ++t)
-                            if (col + t < p.N) p.C[row * p.ldc + col + t] = v[t];
-                    }
-                }
+                store_n<VEC, TI>(p.C, p.ldc, row, col, p.M, p.N, v, interior);
             }
 }
 
-using DefaultCfg = MfmaConfig<128, 128, 16, 2, 2>;
+// Interior kernel: every tile lies wholly inside C, rows of A, B and C are
+// 16-byte aligned, and the slab loop carries no guard at all. The partial
+// last slab (K not a multiple of BK) is loaded once, with guards, after the
+// loop. Same operand order, LDS layout and pipeline as mfma_kernel.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::kThreads)
+__attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mfma_interior_kernel(Problem p,
+                                                                                                 int tiles_m)
+{
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::kThreads;
+    constexpr int MI = Cfg::MI, NJ = Cfg::NJ, TI = Cfg::TI;
+    constexpr int PA = Cfg::kPitchA;
+    constexpr int G = BK / 8;
+    constexpr int CA = Cfg::kChunksA, CB = Cfg::kChunksB;
+    using VecB = typename Vec<TI>::T;
+
+    __shared__ __attribute__((aligned(16))) float As[2][BM * PA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * BN];
+
+    int tm, tn;
+    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, Cfg::kGroupM, tm, tn);
+    const std::int64_t m0 = std::int64_t(tm) * BM;
+    const int n0 = tn * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % 64;
+    const int l32 = lane % 32, h = lane / 32;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
+    const int n_full = p.K / BK;
+
+    floatx16 acc[MI][NJ][TI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+            for (int t = 0; t < TI; ++t) acc[mi][nj][t] = floatx16{};
+
+    // This work-item's chunks: A chunk q is row (q*NT + tid) / (BK/4) of the
+    // tile, columns 4 ((q*NT + tid) % (BK/4)) ..; B chunk q is row
+    // (q*NT + tid) / (BN/4), columns 4 ((q*NT + tid) % (BN/4)) ...
+    const float *ga = p.A + (m0 + tid / (BK / 4)) * p.lda + (tid % (BK / 4)) * 4;
+    const float *gb = p.B + std::int64_t(tid / (BN / 4)) * p.ldb + n0 + (tid % (BN / 4)) * 4;
+    constexpr int kRowStepA = NT / (BK / 4);  // tile rows between consecutive chunks q
+    constexpr int kRowStepB = NT / (BN / 4);
+    static_assert(NT % (BK / 4) == 0 && NT % (BN / 4) == 0, "chunk rows must advance evenly");
+
+    f32x4 ra[CA], rb[CB];
+    auto fetch = [&](int slab) {
+        const std::int64_t ka = std::int64_t(slab) * BK, kb = std::int64_t(slab) * BK * p.ldb;
+#pragma unroll
+        for (int q = 0; q < CA; ++q)
+            ra[q] = *reinterpret_cast<const f32x4 *>(ga + q * kRowStepA * p.lda + ka);
+#pragma unroll
+        for (int q = 0; q < CB; ++q)
+            rb[q] = *reinterpret_cast<const f32x4 *>(gb + q * kRowStepB * p.ldb + kb);
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < CA; ++q) {
+            const int c = q * NT + tid;
+            *reinterpret_cast<f32x4 *>(&As[buf][(c / (BK / 4)) * PA + (c % (BK / 4)) * 4]) = ra[q];
+        }
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            const int c = q * NT + tid;
+            *reinterpret_cast<f32x4 *>(&Bs[buf][(c / (BN / 4)) * BN + (c % (BN / 4)) * 4]) = rb[q];
+        }
+    };
+
+    float4 af[2][MI];
+    VecB bf[2][4][NJ];
+    auto read_frags = [&](int buf, int g, int slot) {
+        const float *as = As[buf];
+        const float *bs = Bs[buf];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+            af[slot][mi] = *reinterpret_cast<const float4 *>(&as[(wm0 + mi * 32 + l32) * PA + 8 * g + 4 * h]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int nj = 0; nj < NJ; ++nj)
+                bf[slot][s][nj] =
+                    *reinterpret_cast<const VecB *>(&bs[(8 * g + 4 * h + s) * BN + wn0 + nj * 32 * TI + l32 * TI]);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+                    for (int t = 0; t < TI; ++t)
+                        acc[mi][nj][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            elem(af[slot][mi], s), elem(bf[slot][s][nj], t), acc[mi][nj][t], 0, 0, 0);
+    };
+    auto multiply = [&](int buf, auto &&between) {
+        read_frags(buf, 0, 0);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (g + 1 < G) read_frags(buf, g + 1, (g + 1) & 1);
+            if (g == G / 2) between();
+            mfmas(g & 1);
+        }
+    };
+
+    if (n_full > 0) {
+        fetch(0);
+        stash(0);
+        if (n_full > 1) fetch(1);
+        __syncthreads();
+        for (int t = 0; t < n_full; ++t) {
+            const int cur = t & 1;
+            multiply(cur, [&] {
+                if (t + 1 < n_full) {
+                    stash(cur ^ 1);
+                    if (t + 2 < n_full) fetch(t + 2);
+                }
+            });
+            __syncthreads();
+        }
+    }
+    if (n_full * BK < p.K) {
+        // Partial last slab: columns k >= K of A and rows k >= K of B read as
+        // zero. Written straight to LDS one element at a time; this runs once.
+        const int k0 = n_full * BK;
+#pragma unroll 1
+        for (int e = tid; e < BM * BK; e += NT) {
+            const int r = e / BK, k = e % BK;
+            As[0][r * PA + k] = k0 + k < p.K ? p.A[(m0 + r) * p.lda + k0 + k] : 0.0f;
+        }
+#pragma unroll 1
+        for (int e = tid; e < BK * BN; e += NT) {
+            const int k = e / BN, c = e % BN;
+            Bs[0][k * BN + c] = k0 + k < p.K ? p.B[std::int64_t(k0 + k) * p.ldb + n0 + c] : 0.0f;
+        }
+        __syncthreads();
+        multiply(0, [] {});
+    }
+
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const std::int64_t row = m0 + wm0 + mi * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                const int col = n0 + wn0 + nj * 32 * TI + l32 * TI;
+                float v[TI];
+#pragma unroll
+                for (int t = 0; t < TI; ++t) v[t] = acc[mi][nj][t][r];
+                store_n<true, TI>(p.C, p.ldc, row, col, p.M, p.N, v, true);
+            }
+}
+
+#ifndef SGEMM_MFMA_TILE
+#define SGEMM_MFMA_TILE 128, 128, 32, 2, 2
+#endif
+#ifndef SGEMM_MFMA_BIG_TILE
+#define SGEMM_MFMA_BIG_TILE 128, 256, 16, 1, 2
+#endif
+// Tile shapes (BM, BN, BK, WAVES_M, WAVES_N): the general kernel (edges,
+// unaligned rows) and the interior kernel.
+using GeneralCfg = MfmaConfig<SGEMM_MFMA_TILE>;
+using InteriorCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
 
 template <class Cfg>
-hipError_t launch_cfg(const Problem &p, hipStream_t stream)
+hipError_t launch_general(const Problem &p, hipStream_t stream)
 {
     const void *kernel = rows_aligned16(p) ? reinterpret_cast<const void *>(&mfma_kernel<Cfg, true>)
                                            : reinterpret_cast<const void *>(&mfma_kernel<Cfg, false>);
@@ -231,8 +459,46 @@ hipError_t launch_cfg(const Problem &p, hipStream_t stream)
     });
 }
 
+// Whole tiles of the interior kernel go to it; the strips left at the bottom
+// (rows beyond the last whole tile row) and on the right (columns beyond the
+// last whole tile column) are themselves products and go to the general
+// kernel. The launches write disjoint parts of C.
+hipError_t launch_split(const Problem &p, hipStream_t stream)
+{
+    using Cfg = InteriorCfg;
+    const std::int64_t mi = std::int64_t(p.M / Cfg::BM) * Cfg::BM;
+    const std::int64_t ni = std::int64_t(p.N / Cfg::BN) * Cfg::BN;
+    if (!rows_aligned16(p) || mi == 0 || ni == 0) return launch_general<GeneralCfg>(p, stream);
+    Problem in = p;
+    in.M = int(mi);
+    in.N = int(ni);
+    hipError_t e = for_each_band<Cfg::BM, Cfg::BN>(in, [&](Problem q, int tiles_m, int tiles_n) {
+        void *args[] = {&q, &tiles_m};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&mfma_interior_kernel<Cfg>),
+                               dim3(unsigned(tiles_m) * unsigned(tiles_n)), dim3(Cfg::kThreads), args, 0, stream);
+    });
+    if (e != hipSuccess) return e;
+    if (mi < p.M) {  // bottom strip, full width
+        Problem q = p;
+        q.M = int(p.M - mi);
+        q.A = p.A + mi * p.lda;
+        q.C = p.C + mi * p.ldc;
+        e = launch_general<GeneralCfg>(q, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (ni < p.N) {  // right strip, above the bottom strip
+        Problem q = p;
+        q.M = int(mi);
+        q.N = int(p.N - ni);
+        q.B = p.B + ni;
+        q.C = p.C + ni;
+        e = launch_general<GeneralCfg>(q, stream);
+    }
+    return e;
+}
+
 }  // namespace
 
-hipError_t launch_mfma(const Problem &p, hipStream_t stream) { return launch_cfg<DefaultCfg>(p, stream); }
+hipError_t launch_mfma(const Problem &p, hipStream_t stream) { return launch_split(p, stream); }
 
 }  // namespace sgemm_impl

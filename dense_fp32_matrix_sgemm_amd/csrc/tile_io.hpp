@@ -37,6 +37,70 @@ __device__ __forceinline__ float4 load4(const float *base, std::int64_t ld, std:
     return v;
 }
 
+// Four consecutive elements known to lie inside the matrix (no guard).
+template <bool VEC>
+__device__ __forceinline__ float4 load4_inside(const float *base, std::int64_t ld, std::int64_t row, int c)
+{
+    const float *p = base + row * ld + c;
+    if constexpr (VEC) {
+        return *reinterpret_cast<const float4 *>(p);
+    } else {
+        return make_float4(p[0], p[1], p[2], p[3]);
+    }
+}
+
+// Four consecutive elements (row, c .. c+3) of which some may lie outside the
+// matrix: every address is clamped into it (rows, cols >= 1), so all four
+// loads are in bounds and unconditional. The values read for outside
+// elements are junk until zero_outside() replaces them; keeping that select
+// away from the loads stops the compiler from turning each load into a
+// branch that waits for its own result.
+__device__ __forceinline__ float4 load4_clamped(const float *base, std::int64_t ld, std::int64_t row, int c,
+                                                std::int64_t rows, int cols)
+{
+    const float *p = base + (row < rows ? row : rows - 1) * ld;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = p[c + e < cols ? c + e : cols - 1];
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Zero the elements of a chunk loaded by load4_clamped that lie outside the
+// rows x cols matrix (the zero padding of ragged tiles).
+__device__ __forceinline__ void zero_outside(float4 &v, std::int64_t row, int c, std::int64_t rows, int cols)
+{
+    const bool r = row < rows;
+    v.x = (r && c + 0 < cols) ? v.x : 0.0f;
+    v.y = (r && c + 1 < cols) ? v.y : 0.0f;
+    v.z = (r && c + 2 < cols) ? v.z : 0.0f;
+    v.w = (r && c + 3 < cols) ? v.w : 0.0f;
+}
+
+// Store N (1, 2 or 4) consecutive floats v[0..N-1] at (row, c ..) of C.
+// `inside` promises the whole run lies in C; with VEC it is then one store
+// of 4N bytes (alignment as for load4). Otherwise elements outside rows x
+// cols are dropped.
+template <bool VEC, int N>
+__device__ __forceinline__ void store_n(float *base, std::int64_t ld, std::int64_t row, int c, std::int64_t rows,
+                                        int cols, const float (&v)[N], bool inside)
+{
+    float *p = base + row * ld + c;
+    if (VEC && inside) {
+        if constexpr (N == 4) {
+            *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (N == 2) {
+            *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+        } else {
+            p[0] = v[0];
+        }
+        return;
+    }
+    if (row >= rows) return;
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        if (c + e < cols) p[e] = v[e];
+}
+
 // Store n (1..4) consecutive floats v[0..n-1] at (row, c ..) of C, dropping
 // elements outside rows x cols. With VEC and all four inside, one 16-byte
 // store (same alignment contract as load4).

@@ -90,6 +90,25 @@ def test_tile_edges(variant):
         assert_within(gemm(A, B, variant), Cref, S, f"{variant} {M}x{N}x{K}")
 
 
+# Aligned shapes that are not whole multiples of the largest tiles: the MFMA
+# path then splits the product into whole interior tiles plus bottom and
+# right strips (also K tails that are not whole slabs).
+SPLIT = [(1000, 1000, 1000), (520, 776, 336), (384, 512, 20), (129, 260, 4100),
+         (256, 4, 64), (4, 256, 8), (2048, 1280, 1028)]
+
+
+@pytest.mark.parametrize("variant", ["mfma", "best"])
+def test_interior_and_strip_split(variant):
+    _announce(f"interior/strip split variant {variant}")
+    for (M, N, K) in SPLIT:
+        A, B = synth.operands(M, N, K, "pm1", seed_a=M + 1, seed_b=N + K + 1)
+        Cref, S = oracle.gemm(A, B, with_abs=True)
+        assert_within(gemm(A, B, variant), Cref, S, f"{variant} {M}x{N}x{K}")
+        Ai = synth.small_int(M, (M, K))
+        Bi = synth.small_int(N, (K, N))
+        assert np.array_equal(gemm(Ai, Bi, variant).astype(np.float64), oracle.gemm(Ai, Bi))
+
+
 @pytest.mark.parametrize("variant", VARIANTS[:4])
 @pytest.mark.parametrize("shape", [(300, 257, 513), (3001, 2047, 4093), (1024, 1024, 1024)])
 def test_small_integers_bit_exact(variant, shape):
