@@ -93,6 +93,9 @@ struct MfmaConfig {
     static constexpr std::size_t kLdsBytes = sizeof(float) * 2 * (BM * kPitchA + BK * BN);
 };
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+
 template <class Cfg, bool VEC>
 __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tiles_m)
 {
@@ -281,7 +284,14 @@ __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tile
 // Interior kernel: every tile lies wholly inside C, rows of A, B and C are
 // 16-byte aligned, and the slab loop carries no guard at all. The partial
 // last slab (K not a multiple of BK) is loaded once, with guards, after the
-// loop. Same operand order, LDS layout and pipeline as mfma_kernel.
+// loop. Same operand order and LDS layout as mfma_kernel; the slab loop is
+// arranged for a single wave per SIMD:
+//  * each steady-state slab is one straight-line block whose LDS stores,
+//    global loads and fragment reads are spread one per MFMA (a burst of
+//    memory instructions would hold back the next MFMA, as a wave issues in
+//    order);
+//  * the barrier sits before the last group of k of the slab, so the first
+//    fragments of the next slab load while that group is multiplied.
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::kThreads)
 __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mfma_interior_kernel(Problem p,
@@ -387,21 +397,80 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mf
         }
     };
 
-    if (n_full > 0) {
+    static_assert(G % 2 == 0, "the pipelined loop needs an even number of k-groups per slab");
+    constexpr int NR = MI + 4 * NJ;            // fragment reads per group
+    // Interleave hints: one memory instruction after each MFMA, so no burst
+    // of loads or stores holds back the next MFMA in the wave's in-order issue.
+    auto interleave_a = [&] {
+#pragma unroll
+        for (int i = 0; i < (G - 1) * NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < CA + CB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < CA + CB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        }
+    };
+    auto interleave_b = [&] {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+    };
+
+    const int n = n_full;
+    if (n > 0) {
         fetch(0);
         stash(0);
-        if (n_full > 1) fetch(1);
+        if (n > 1) fetch(1);
         __syncthreads();
-        for (int t = 0; t < n_full; ++t) {
+        read_frags(0, 0, 0);
+        int t = 0;
+        // Steady state, one straight-line block per slab t (LDS buffer cur):
+        //   A: store slab t+1 (registers) to buffer cur^1, start loading slab
+        //      t+2, read groups 1..G-1 of slab t while multiplying groups
+        //      0..G-2;
+        //   barrier: slab t+1 is complete in LDS, and every wave has finished
+        //      reading buffer cur^1's previous contents (slab t-1, before the
+        //      previous barrier);
+        //   B: read group 0 of slab t+1 while multiplying group G-1 of slab t.
+        for (; t + 2 < n; ++t) {
             const int cur = t & 1;
-            multiply(cur, [&] {
-                if (t + 1 < n_full) {
-                    stash(cur ^ 1);
-                    if (t + 2 < n_full) fetch(t + 2);
-                }
-            });
+            stash(cur ^ 1);
+            fetch(t + 2);
+#pragma unroll
+            for (int g = 0; g + 1 < G; ++g) {
+                read_frags(cur, g + 1, (g + 1) & 1);
+                mfmas(g & 1);
+            }
+            interleave_a();
             __syncthreads();
+            read_frags(cur ^ 1, 0, 0);
+            mfmas((G - 1) & 1);
+            interleave_b();
         }
+        // Last two slabs: no more loads.
+        for (; t < n; ++t) {
+            const int cur = t & 1;
+            if (t + 1 < n) stash(cur ^ 1);
+#pragma unroll
+            for (int g = 0; g + 1 < G; ++g) {
+                read_frags(cur, g + 1, (g + 1) & 1);
+                mfmas(g & 1);
+            }
+            __syncthreads();
+            if (t + 1 < n) read_frags(cur ^ 1, 0, 0);
+            mfmas((G - 1) & 1);
+        }
+        __syncthreads();
     }
     if (n_full * BK < p.K) {
         // Partial last slab: columns k >= K of A and rows k >= K of B read as
@@ -440,7 +509,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mf
 #define SGEMM_MFMA_TILE 128, 128, 32, 2, 2
 #endif
 #ifndef SGEMM_MFMA_BIG_TILE
-#define SGEMM_MFMA_BIG_TILE 128, 256, 16, 1, 2
+#define SGEMM_MFMA_BIG_TILE 256, 256, 16, 2, 2
 #endif
 // Tile shapes (BM, BN, BK, WAVES_M, WAVES_N): the general kernel (edges,
 // unaligned rows) and the interior kernel.
