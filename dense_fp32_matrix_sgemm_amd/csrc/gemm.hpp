@@ -15,6 +15,7 @@ struct Problem {
     float *C;
     std::int64_t lda, ldb, ldc;
     int M, N, K;
+    int cus;  // compute units of the device (for the choice of tile size)
 };
 
 // Each launcher enqueues the variant's kernel(s) on `stream` and returns the

@@ -75,6 +75,7 @@ struct MfmaConfig {
     static constexpr int NJ = WN / (32 * TI);
     static constexpr int kPadA = 4;
     static constexpr int kPitchA = BK + kPadA;
+    static constexpr int kLdsFloats = 2 * (BM * kPitchA + BK * BN);  // two stages of A and B tiles
     static constexpr int kChunksA = BM * BK / 4 / kThreads;  // 4-wide chunks per work-item
     static constexpr int kChunksB = BK * BN / 4 / kThreads;
 #ifndef SGEMM_MFMA_GROUP_M
@@ -82,8 +83,8 @@ struct MfmaConfig {
 #endif
     static constexpr int kGroupM = SGEMM_MFMA_GROUP_M;
     // Waves per SIMD the register allocation aims at: one when a wave's
-    // accumulators alone fill the 256 AGPRs, two otherwise.
-    static constexpr int kWavesPerEU = MI * NJ * TI * 16 >= 256 ? 1 : 2;
+    // accumulators alone fill the 256 AGPRs, more as they shrink.
+    static constexpr int kWavesPerEU = MI * NJ * TI * 16 >= 256 ? 1 : MI * NJ * TI * 16 >= 64 ? 2 : 4;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(TI == 1 || TI == 2 || TI == 4, "column interleave must be 1, 2 or 4");
     static_assert(WN == 32 * TI * NJ, "wave tile width must split into interleaved groups");
@@ -96,8 +97,10 @@ struct MfmaConfig {
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
 
+// One BM x BN tile (tm, tn) of the product p, with guards on every edge;
+// `lds` holds Cfg::kLdsFloats floats.
 template <class Cfg, bool VEC>
-__global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tiles_m)
+__device__ __forceinline__ void general_tile(const Problem &p, int tm, int tn, float *lds)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
     constexpr int MI = Cfg::MI, NJ = Cfg::NJ, TI = Cfg::TI;
@@ -105,11 +108,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tile
     constexpr int G = BK / 8;  // groups of 8 k per slab
     using VecB = typename Vec<TI>::T;
 
-    __shared__ __attribute__((aligned(16))) float As[2][BM * PA];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK * BN];
+    float(*As)[BM * PA] = reinterpret_cast<float(*)[BM * PA]>(lds);
+    float(*Bs)[BK * BN] = reinterpret_cast<float(*)[BK * BN]>(lds + 2 * BM * PA);
 
-    int tm, tn;
-    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, Cfg::kGroupM, tm, tn);
     const std::int64_t m0 = std::int64_t(tm) * BM;
     const int n0 = tn * BN;
 
@@ -281,10 +282,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tile
             }
 }
 
-// Interior kernel: every tile lies wholly inside C, rows of A, B and C are
-// 16-byte aligned, and the slab loop carries no guard at all. The partial
+// Interior tiles: the tile lies wholly inside C and the slab loop carries
+// no guard at all. Rows need only the 4-byte alignment of any float: global
+// memory moves in 16-byte accesses that gfx950 performs unaligned. The partial
 // last slab (K not a multiple of BK) is loaded once, with guards, after the
-// loop. Same operand order and LDS layout as mfma_kernel; the slab loop is
+// loop. Same operand order and LDS layout as general_tile; the slab loop is
 // arranged for a single wave per SIMD:
 //  * each steady-state slab is one straight-line block whose LDS stores,
 //    global loads and fragment reads are spread one per MFMA (a burst of
@@ -292,10 +294,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tile
 //    order);
 //  * the barrier sits before the last group of k of the slab, so the first
 //    fragments of the next slab load while that group is multiplied.
+// interior_tile computes one whole BM x BN tile (tm, tn) of the product p
+// (no edge inside it); `lds` holds Cfg::kLdsFloats floats.
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::kThreads)
-__attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mfma_interior_kernel(Problem p,
-                                                                                                 int tiles_m)
+__device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, float *lds)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::kThreads;
     constexpr int MI = Cfg::MI, NJ = Cfg::NJ, TI = Cfg::TI;
@@ -304,11 +306,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mf
     constexpr int CA = Cfg::kChunksA, CB = Cfg::kChunksB;
     using VecB = typename Vec<TI>::T;
 
-    __shared__ __attribute__((aligned(16))) float As[2][BM * PA];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK * BN];
+    float(*As)[BM * PA] = reinterpret_cast<float(*)[BM * PA]>(lds);
+    float(*Bs)[BK * BN] = reinterpret_cast<float(*)[BK * BN]>(lds + 2 * BM * PA);
 
-    int tm, tn;
-    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, Cfg::kGroupM, tm, tn);
     const std::int64_t m0 = std::int64_t(tm) * BM;
     const int n0 = tn * BN;
 
@@ -342,10 +342,10 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mf
         const std::int64_t ka = std::int64_t(slab) * BK, kb = std::int64_t(slab) * BK * p.ldb;
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            ra[q] = *reinterpret_cast<const f32x4 *>(ga + q * kRowStepA * p.lda + ka);
+            ra[q] = load16u(ga + q * kRowStepA * p.lda + ka);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            rb[q] = *reinterpret_cast<const f32x4 *>(gb + q * kRowStepB * p.ldb + kb);
+            rb[q] = load16u(gb + q * kRowStepB * p.ldb + kb);
     };
     auto stash = [&](int buf) {
 #pragma unroll
@@ -498,10 +498,14 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mf
             for (int r = 0; r < 16; ++r) {
                 const std::int64_t row = m0 + wm0 + mi * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                 const int col = n0 + wn0 + nj * 32 * TI + l32 * TI;
-                float v[TI];
-#pragma unroll
-                for (int t = 0; t < TI; ++t) v[t] = acc[mi][nj][t][r];
-                store_n<true, TI>(p.C, p.ldc, row, col, p.M, p.N, v, true);
+                float *c = p.C + row * p.ldc + col;
+                if constexpr (TI == 4) {
+                    store16u(c, f32x4{acc[mi][nj][0][r], acc[mi][nj][1][r], acc[mi][nj][2][r], acc[mi][nj][3][r]});
+                } else if constexpr (TI == 2) {
+                    store8u(c, acc[mi][nj][0][r], acc[mi][nj][1][r]);
+                } else {
+                    c[0] = acc[mi][nj][0][r];
+                }
             }
 }
 
@@ -511,10 +515,82 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mf
 #ifndef SGEMM_MFMA_BIG_TILE
 #define SGEMM_MFMA_BIG_TILE 256, 256, 16, 2, 2
 #endif
-// Tile shapes (BM, BN, BK, WAVES_M, WAVES_N): the general kernel (edges,
-// unaligned rows) and the interior kernel.
+#ifndef SGEMM_MFMA_MID_TILE
+#define SGEMM_MFMA_MID_TILE 128, 128, 32, 2, 2
+#endif
+#ifndef SGEMM_MFMA_SMALL_TILE
+#define SGEMM_MFMA_SMALL_TILE 64, 64, 32, 2, 2
+#endif
+// Tile shapes (BM, BN, BK, WAVES_M, WAVES_N): the general tiles (edges) and
+// three sizes of interior tile.
 using GeneralCfg = MfmaConfig<SGEMM_MFMA_TILE>;
-using InteriorCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
+using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
+using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
+using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
+
+template <class A, class B>
+constexpr int max_lds() { return A::kLdsFloats > B::kLdsFloats ? A::kLdsFloats : B::kLdsFloats; }
+
+// Products too small for a single interior tile: general tiles only.
+template <class Cfg, bool VEC>
+__global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tiles_m)
+{
+    __shared__ __attribute__((aligned(16))) float lds[Cfg::kLdsFloats];
+    int tm, tn;
+    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, Cfg::kGroupM, tm, tn);
+    general_tile<Cfg, VEC>(p, tm, tn, lds);
+}
+
+// Work-group layout of one fused launch: first the interior tiles (whole
+// ICfg tiles covering rows [0, mi) and columns [0, ni)), then the general
+// tiles of the bottom strip (rows [mi, M), all columns) and of the right
+// strip (rows [0, mi), columns [ni, N)).
+struct FusedGrid {
+    unsigned n_interior, n_bottom;
+    int tiles_m;              // interior tile rows
+    int bottom_tn, right_tn;  // general tiles per row of each strip
+    int mi, ni;
+};
+
+// One launch for the whole product, so the small strips run beside the
+// interior tiles instead of after them; the two bodies share one LDS buffer.
+template <class A, class B>
+constexpr int min_waves() { return A::kWavesPerEU < B::kWavesPerEU ? A::kWavesPerEU : B::kWavesPerEU; }
+
+template <class ICfg, class GCfg, bool VEC>
+__global__ __launch_bounds__(ICfg::kThreads)
+__attribute__((amdgpu_waves_per_eu(min_waves<ICfg, GCfg>(), min_waves<ICfg, GCfg>()))) void mfma_fused_kernel(
+    Problem p, FusedGrid g)
+{
+    static_assert(ICfg::kThreads == GCfg::kThreads, "both bodies run in the same work-group shape");
+    __shared__ __attribute__((aligned(16))) float lds[max_lds<ICfg, GCfg>()];
+    const unsigned w = blockIdx.x;
+    if (w < g.n_interior) {
+        int tm, tn;
+        tile_of_workgroup(w, g.n_interior, g.tiles_m, ICfg::kGroupM, tm, tn);
+        interior_tile<ICfg>(p, tm, tn, lds);
+        return;
+    }
+    unsigned e = w - g.n_interior;
+    Problem q = p;
+    int tm, tn;
+    if (e < g.n_bottom) {
+        q.M = p.M - g.mi;
+        if (p.K > 0) q.A = p.A + std::int64_t(g.mi) * p.lda;
+        q.C = p.C + std::int64_t(g.mi) * p.ldc;
+        tm = int(e / unsigned(g.bottom_tn));
+        tn = int(e % unsigned(g.bottom_tn));
+    } else {
+        e -= g.n_bottom;
+        q.M = g.mi;
+        q.N = p.N - g.ni;
+        if (p.K > 0) q.B = p.B + g.ni;
+        q.C = p.C + g.ni;
+        tm = int(e / unsigned(g.right_tn));
+        tn = int(e % unsigned(g.right_tn));
+    }
+    general_tile<GCfg, VEC>(q, tm, tn, lds);
+}
 
 template <class Cfg>
 hipError_t launch_general(const Problem &p, hipStream_t stream)
@@ -528,46 +604,51 @@ hipError_t launch_general(const Problem &p, hipStream_t stream)
     });
 }
 
-// Whole tiles of the interior kernel go to it; the strips left at the bottom
-// (rows beyond the last whole tile row) and on the right (columns beyond the
-// last whole tile column) are themselves products and go to the general
-// kernel. The launches write disjoint parts of C.
-hipError_t launch_split(const Problem &p, hipStream_t stream)
+template <class Cfg>
+std::int64_t whole_tiles(const Problem &p)
 {
-    using Cfg = InteriorCfg;
-    const std::int64_t mi = std::int64_t(p.M / Cfg::BM) * Cfg::BM;
-    const std::int64_t ni = std::int64_t(p.N / Cfg::BN) * Cfg::BN;
-    if (!rows_aligned16(p) || mi == 0 || ni == 0) return launch_general<GeneralCfg>(p, stream);
-    Problem in = p;
-    in.M = int(mi);
-    in.N = int(ni);
-    hipError_t e = for_each_band<Cfg::BM, Cfg::BN>(in, [&](Problem q, int tiles_m, int tiles_n) {
-        void *args[] = {&q, &tiles_m};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&mfma_interior_kernel<Cfg>),
-                               dim3(unsigned(tiles_m) * unsigned(tiles_n)), dim3(Cfg::kThreads), args, 0, stream);
+    return std::int64_t(p.M / Cfg::BM) * std::int64_t(p.N / Cfg::BN);
+}
+
+template <class ICfg, class GCfg>
+hipError_t launch_fused(const Problem &p, hipStream_t stream)
+{
+    return for_each_band<ICfg::BM, ICfg::BN>(p, [&](Problem q, int, int) {
+        const int mi = q.M / ICfg::BM * ICfg::BM, ni = q.N / ICfg::BN * ICfg::BN;
+        if (mi == 0 || ni == 0) return launch_general<GeneralCfg>(q, stream);
+        FusedGrid g;
+        g.tiles_m = mi / ICfg::BM;
+        g.n_interior = unsigned(g.tiles_m) * unsigned(ni / ICfg::BN);
+        g.mi = mi;
+        g.ni = ni;
+        g.bottom_tn = (q.N + GCfg::BN - 1) / GCfg::BN;
+        g.right_tn = (q.N - ni + GCfg::BN - 1) / GCfg::BN;
+        g.n_bottom = mi < q.M ? unsigned((q.M - mi + GCfg::BM - 1) / GCfg::BM) * unsigned(g.bottom_tn) : 0u;
+        const unsigned n_right = ni < q.N ? unsigned((mi + GCfg::BM - 1) / GCfg::BM) * unsigned(g.right_tn) : 0u;
+        const void *kernel = rows_aligned16(q) ? reinterpret_cast<const void *>(&mfma_fused_kernel<ICfg, GCfg, true>)
+                                               : reinterpret_cast<const void *>(&mfma_fused_kernel<ICfg, GCfg, false>);
+        void *args[] = {&q, &g};
+        return hipLaunchKernel(kernel, dim3(g.n_interior + g.n_bottom + n_right), dim3(ICfg::kThreads), args, 0,
+                               stream);
     });
-    if (e != hipSuccess) return e;
-    if (mi < p.M) {  // bottom strip, full width
-        Problem q = p;
-        q.M = int(p.M - mi);
-        q.A = p.A + mi * p.lda;
-        q.C = p.C + mi * p.ldc;
-        e = launch_general<GeneralCfg>(q, stream);
-        if (e != hipSuccess) return e;
-    }
-    if (ni < p.N) {  // right strip, above the bottom strip
-        Problem q = p;
-        q.M = int(mi);
-        q.N = int(p.N - ni);
-        q.B = p.B + ni;
-        q.C = p.C + ni;
-        e = launch_general<GeneralCfg>(q, stream);
-    }
-    return e;
+}
+
+// Tile size by shape: the largest interior tile whose whole tiles alone
+// give every compute unit at least one work-group (one 256x256 tile per CU
+// already keeps all four SIMDs of the CU busy); smaller products fall back
+// to 128x128 and then 64x64 tiles, which trade operand reuse for parallelism.
+// The strips of a 256x256 split use 128x128 general tiles; the smaller
+// splits use general tiles of their own size.
+hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
+{
+    const std::int64_t fill = p.cus > 0 ? p.cus : 256;
+    if (whole_tiles<BigCfg>(p) >= fill) return launch_fused<BigCfg, GeneralCfg>(p, stream);
+    if (whole_tiles<MidCfg>(p) >= fill) return launch_fused<MidCfg, MidCfg>(p, stream);
+    return launch_fused<SmallCfg, SmallCfg>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_mfma(const Problem &p, hipStream_t stream) { return launch_split(p, stream); }
+hipError_t launch_mfma(const Problem &p, hipStream_t stream) { return launch_by_shape(p, stream); }
 
 }  // namespace sgemm_impl

@@ -37,6 +37,22 @@ __device__ __forceinline__ float4 load4(const float *base, std::int64_t ld, std:
     return v;
 }
 
+// 16 bytes at a float address that need only be 4-byte aligned. gfx950 has
+// unaligned global access, so this is still a single 128-bit load or store.
+typedef float f32x4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4u load16u(const float *p)
+{
+    f32x4u v;
+    __builtin_memcpy(&v, p, sizeof(v));
+    return v;
+}
+__device__ __forceinline__ void store16u(float *p, f32x4u v) { __builtin_memcpy(p, &v, sizeof(v)); }
+__device__ __forceinline__ void store8u(float *p, float a, float b)
+{
+    const float v[2] = {a, b};
+    __builtin_memcpy(p, v, sizeof(v));
+}
+
 // Four consecutive elements known to lie inside the matrix (no guard).
 template <bool VEC>
 __device__ __forceinline__ float4 load4_inside(const float *base, std::int64_t ld, std::int64_t row, int c)
