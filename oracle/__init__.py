@@ -1,4 +1,5 @@
-"""CPU oracle for C = A * B (float32 inputs, double accumulation).
+"""CPU oracle for C = A * B and C = alpha * op(A) * op(B) + beta * C
+(float32 inputs, double accumulation).
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg use it; the library never does. It is a thin ctypes wrapper
@@ -37,6 +38,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_gemm.restype = ctypes.c_int
     lib.oracle_gemm_entries.argtypes = [i64, vp, vp, i64, vp, i64, vp, i64, vp, vp]
     lib.oracle_gemm_entries.restype = ctypes.c_int
+    d = ctypes.c_double
+    lib.oracle_gemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, d, vp, i64, vp, i64, d,
+                                   vp, i64, vp, i64, vp, i64]
+    lib.oracle_gemm_ex.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -114,6 +119,42 @@ def gemm_entries(A: np.ndarray, B: np.ndarray, rows, cols, lib=None):
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_entries returned {rc}")
     return out, sabs
+
+
+def gemm_ex(transA: bool, transB: bool, alpha: float, A: np.ndarray, B: np.ndarray,
+            beta: float, C: np.ndarray | None, lib=None):
+    """(alpha * op(A) @ op(B) + beta * C, error scale S) in double.
+
+    A is stored M x K (or K x M when transA), B K x N (or N x K when transB);
+    C (M x N float32) is read only when beta != 0.
+    """
+    lib = lib or load()
+    if transA:
+        K, M = A.shape
+    else:
+        M, K = A.shape
+    if transB:
+        N, K2 = B.shape
+    else:
+        K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    pa, lda = _rows_view(A, *A.shape)
+    pb, ldb = _rows_view(B, *B.shape)
+    if beta != 0.0:
+        if C is None or C.shape != (M, N):
+            raise ValueError("C must be M x N when beta != 0")
+        pc, ldc = _rows_view(C, M, N)
+    else:
+        pc, ldc = None, max(N, 1)
+    out = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64)
+    rc = lib.oracle_gemm_ex(int(bool(transA)), int(bool(transB)), M, N, K, float(alpha),
+                            pa, max(lda, 1), pb, max(ldb, 1), float(beta), pc, max(ldc, 1),
+                            out.ctypes.data, max(N, 1), S.ctypes.data, max(N, 1))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_ex returned {rc}")
+    return out, S
 
 
 def num_threads(lib=None) -> int:

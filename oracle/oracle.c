@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the FP32 matrix product C = A * B.
+ * CPU oracle for the FP32 matrix product C = A * B and its general form
+ * C = alpha * op(A) * op(B) + beta * C.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing in the library calls this; only the test
  * suite, the smoke check and the benchmark's CPU-baseline leg load it. It
@@ -20,6 +21,9 @@
  *
  * Alongside C the oracle can return S[i][j] = sum_k |A[i][k]| * |B[k][j]|,
  * which scales the elementwise error bound of a float32 result.
+ *
+ * oracle_gemm_ex adds the scalars and transpose flags of the BLAS-style call
+ * (C = alpha * op(A) * op(B) + beta * C) with the same per-element order.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math: the sums must not
  * be reassociated).
@@ -85,6 +89,44 @@ int oracle_gemm_entries(int64_t n, const int64_t *rows, const int64_t *cols,
         }
         out[e] = acc;
         if (sabs) sabs[e] = accabs;
+    }
+    return 0;
+}
+
+/* The general form C = alpha * op(A) * op(B) + beta * C of the vendor call
+ * on "Matrix Multiplication -- Naive to Tiled", section 07 (where alpha = 1,
+ * beta = 0), with op(X) = X or its transpose:
+ *   op(A) is M x K: transA == 0 reads A[i][k] = A[i*lda + k] (A stored M x K),
+ *                   transA != 0 reads A[k][i] = A[k*lda + i] (A stored K x M);
+ *   op(B) is K x N: transB == 0 reads B[k*ldb + j] (B stored K x N),
+ *                   transB != 0 reads B[j*ldb + k] (B stored N x K).
+ * C_in (M x N float, leading dimension ldc_in) is read only when beta != 0;
+ * A and B only when alpha != 0. Out (double) receives the result and, when
+ * Sout is not NULL, Sout receives |alpha| * sum_k |op(A)[i][k]| |op(B)[k][j]|
+ * + |beta * C_in[i][j]|, the scale of the rounding error of a float result.
+ * Each sum runs in ascending k, in double. */
+int oracle_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
+                   const float *A, int64_t lda, const float *B, int64_t ldb, double beta,
+                   const float *C_in, int64_t ldc_in, double *Out, int64_t ldo, double *Sout, int64_t lds)
+{
+    if (M < 0 || N < 0 || K < 0) return -1;
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = 0.0, accabs = 0.0;
+            if (alpha != 0.0) {
+                for (int64_t k = 0; k < K; ++k) {
+                    const double a = (double)(transA ? A[k * lda + i] : A[i * lda + k]);
+                    const double b = (double)(transB ? B[j * ldb + k] : B[k * ldb + j]);
+                    acc += a * b;
+                    accabs += absd(a) * absd(b);
+                }
+            }
+            const double c = beta != 0.0 ? beta * (double)C_in[i * ldc_in + j] : 0.0;
+            Out[i * ldo + j] = alpha * acc + c;
+            if (Sout) Sout[i * lds + j] = absd(alpha) * accabs + absd(c);
+        }
     }
     return 0;
 }

@@ -2,7 +2,8 @@
 
 Each case plants one mistake in a copy of ``oracle/oracle.c`` (a dropped term,
 a wrong index, a transposed or mis-strided operand, float instead of double
-accumulation, a lost absolute value, a sign error), builds it with gcc into a
+accumulation, a lost absolute value, a sign error, a lost alpha or beta
+term), builds it with gcc into a
 temporary library, and runs the pin battery of ``test_oracle.py`` against it:
 at least one pin must fail. Every planted mistake keeps all memory accesses in
 bounds, so a mutant can only give wrong numbers, never crash the test.
@@ -14,6 +15,7 @@ import pytest
 
 import oracle
 from tests import test_oracle as pins
+from tests import test_oracle_ex as pins_ex
 
 with open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")) as f:
     SOURCE = f.read()
@@ -44,6 +46,17 @@ MUTANTS = {
     "entries_transposed_B": (
         "const double b = (double)B[k * ldb + j];",
         "const double b = (double)B[(k % (j + 1)) * ldb + j];"),
+    # Mistakes in the general form alpha * op(A) * op(B) + beta * C.
+    "ex_drops_beta_term": ("Out[i * ldo + j] = alpha * acc + c;", "Out[i * ldo + j] = alpha * acc;"),
+    "ex_beta_sign": ("Out[i * ldo + j] = alpha * acc + c;", "Out[i * ldo + j] = alpha * acc - c;"),
+    "ex_ignores_alpha": ("Out[i * ldo + j] = alpha * acc + c;", "Out[i * ldo + j] = acc + c;"),
+    "ex_C_stride_ignores_ld": ("beta * (double)C_in[i * ldc_in + j]", "beta * (double)C_in[i * N + j]"),
+    "ex_transA_stride_ignores_ld": ("(transA ? A[k * lda + i] :", "(transA ? A[k * M + i] :"),
+    "ex_transB_neighbour_k": ("B[j * ldb + k] : B[k * ldb + j]", "B[j * ldb + (k + 1) % K] : B[k * ldb + j]"),
+    "ex_transA_ignored": ("(transA ? A[k * lda + i] : A[i * lda + k])",
+                          "(transA ? A[(k % M) * lda + (i % K)] : A[i * lda + k])"),
+    "ex_scale_drops_c": ("absd(alpha) * accabs + absd(c);", "absd(alpha) * accabs;"),
+    "ex_scale_signed_alpha": ("absd(alpha) * accabs + absd(c);", "alpha * accabs + absd(c);"),
 }
 
 
@@ -65,6 +78,18 @@ def _battery(lib):
         (pins.test_agrees_with_numpy_float64, dict(n=128)),
         (pins.test_leading_dimensions_never_read_padding, {}),
         (pins.test_entries_match_full_product_bitwise, {}),
+    ]
+    for (M, N, K) in pins_ex.TINY[:4]:
+        for tA, tB in pins_ex.PAIRS:
+            cases.append((pins_ex.test_ex_exact_brute_force_tiny,
+                          dict(M=M, N=N, K=K, transA=tA, transB=tB)))
+    for tA, tB in pins_ex.PAIRS:
+        cases.append((pins_ex.test_ex_small_integers_exact, dict(transA=tA, transB=tB)))
+        cases.append((pins_ex.test_ex_leading_dimensions_never_read_padding, dict(transA=tA, transB=tB)))
+    cases += [
+        (pins_ex.test_ex_beta_zero_never_reads_C, {}),
+        (pins_ex.test_ex_alpha_zero_never_reads_A_or_B, {}),
+        (pins_ex.test_ex_plain_form_is_the_plain_product, {}),
     ]
     failed = []
     for fn, kw in cases:
