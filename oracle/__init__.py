@@ -42,6 +42,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_gemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, d, vp, i64, vp, i64, d,
                                    vp, i64, vp, i64, vp, i64]
     lib.oracle_gemm_ex.restype = ctypes.c_int
+    lib.oracle_gemm_ex_entries.argtypes = [ctypes.c_int, ctypes.c_int, i64, vp, vp, i64, d, vp, i64, vp, i64,
+                                           d, vp, i64, vp, vp]
+    lib.oracle_gemm_ex_entries.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -154,6 +157,39 @@ def gemm_ex(transA: bool, transB: bool, alpha: float, A: np.ndarray, B: np.ndarr
                             out.ctypes.data, max(N, 1), S.ctypes.data, max(N, 1))
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_ex returned {rc}")
+    return out, S
+
+
+def gemm_ex_entries(transA: bool, transB: bool, alpha: float, A: np.ndarray, B: np.ndarray,
+                    beta: float, C: np.ndarray | None, rows, cols, lib=None):
+    """Selected elements (rows[e], cols[e]) of gemm_ex's result and their
+    error scales, each formed exactly as gemm_ex forms it."""
+    lib = lib or load()
+    M, K = (A.shape[1], A.shape[0]) if transA else A.shape
+    N, K2 = (B.shape[0], B.shape[1]) if transB else (B.shape[1], B.shape[0])
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape or rows.ndim != 1:
+        raise ValueError("rows and cols must be 1-D and of equal length")
+    if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
+        raise IndexError("entry outside the M x N result")
+    pa, lda = _rows_view(A, *A.shape)
+    pb, ldb = _rows_view(B, *B.shape)
+    if beta != 0.0:
+        if C is None or C.shape != (M, N):
+            raise ValueError("C must be M x N when beta != 0")
+        pc, ldc = _rows_view(C, M, N)
+    else:
+        pc, ldc = None, 1
+    out = np.empty(rows.size, dtype=np.float64)
+    S = np.empty(rows.size, dtype=np.float64)
+    rc = lib.oracle_gemm_ex_entries(int(bool(transA)), int(bool(transB)), rows.size, rows.ctypes.data,
+                                    cols.ctypes.data, K, float(alpha), pa, max(lda, 1), pb, max(ldb, 1),
+                                    float(beta), pc, max(ldc, 1), out.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_ex_entries returned {rc}")
     return out, S
 
 

@@ -101,10 +101,30 @@ int oracle_gemm_entries(int64_t n, const int64_t *rows, const int64_t *cols,
  *   op(B) is K x N: transB == 0 reads B[k*ldb + j] (B stored K x N),
  *                   transB != 0 reads B[j*ldb + k] (B stored N x K).
  * C_in (M x N float, leading dimension ldc_in) is read only when beta != 0;
- * A and B only when alpha != 0. Out (double) receives the result and, when
- * Sout is not NULL, Sout receives |alpha| * sum_k |op(A)[i][k]| |op(B)[k][j]|
- * + |beta * C_in[i][j]|, the scale of the rounding error of a float result.
+ * A and B only when alpha != 0. The result of element (i, j) is
+ * alpha * sum_k op(A)[i][k] op(B)[k][j] + beta * C_in[i][j], and its error
+ * scale is |alpha| * sum_k |op(A)[i][k]| |op(B)[k][j]| + |beta * C_in[i][j]|.
  * Each sum runs in ascending k, in double. */
+static void ex_element(int transA, int transB, int64_t i, int64_t j, int64_t K, double alpha, const float *A,
+                       int64_t lda, const float *B, int64_t ldb, double beta, const float *C_in, int64_t ldc_in,
+                       double *out, double *scale)
+{
+    double acc = 0.0, accabs = 0.0;
+    if (alpha != 0.0) {
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = (double)(transA ? A[k * lda + i] : A[i * lda + k]);
+            const double b = (double)(transB ? B[j * ldb + k] : B[k * ldb + j]);
+            acc += a * b;
+            accabs += absd(a) * absd(b);
+        }
+    }
+    const double c = beta != 0.0 ? beta * (double)C_in[i * ldc_in + j] : 0.0;
+    *out = alpha * acc + c;
+    *scale = absd(alpha) * accabs + absd(c);
+}
+
+/* The whole M x N result into Out (double, leading dimension ldo) and, when
+ * Sout is not NULL, the error scales into Sout (leading dimension lds). */
 int oracle_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, double alpha,
                    const float *A, int64_t lda, const float *B, int64_t ldb, double beta,
                    const float *C_in, int64_t ldc_in, double *Out, int64_t ldo, double *Sout, int64_t lds)
@@ -114,19 +134,27 @@ int oracle_gemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, doub
 #pragma omp parallel for schedule(static)
     for (i = 0; i < M; ++i) {
         for (int64_t j = 0; j < N; ++j) {
-            double acc = 0.0, accabs = 0.0;
-            if (alpha != 0.0) {
-                for (int64_t k = 0; k < K; ++k) {
-                    const double a = (double)(transA ? A[k * lda + i] : A[i * lda + k]);
-                    const double b = (double)(transB ? B[j * ldb + k] : B[k * ldb + j]);
-                    acc += a * b;
-                    accabs += absd(a) * absd(b);
-                }
-            }
-            const double c = beta != 0.0 ? beta * (double)C_in[i * ldc_in + j] : 0.0;
-            Out[i * ldo + j] = alpha * acc + c;
-            if (Sout) Sout[i * lds + j] = absd(alpha) * accabs + absd(c);
+            double s;
+            ex_element(transA, transB, i, j, K, alpha, A, lda, B, ldb, beta, C_in, ldc_in, &Out[i * ldo + j], &s);
+            if (Sout) Sout[i * lds + j] = s;
         }
+    }
+    return 0;
+}
+
+/* Selected elements: Out[e] (and Sout[e] when not NULL) for element
+ * (rows[e], cols[e]) of oracle_gemm_ex's result, formed the same way. */
+int oracle_gemm_ex_entries(int transA, int transB, int64_t n, const int64_t *rows, const int64_t *cols, int64_t K,
+                           double alpha, const float *A, int64_t lda, const float *B, int64_t ldb, double beta,
+                           const float *C_in, int64_t ldc_in, double *Out, double *Sout)
+{
+    if (n < 0 || K < 0) return -1;
+    int64_t e;
+#pragma omp parallel for schedule(static)
+    for (e = 0; e < n; ++e) {
+        double s;
+        ex_element(transA, transB, rows[e], cols[e], K, alpha, A, lda, B, ldb, beta, C_in, ldc_in, &Out[e], &s);
+        if (Sout) Sout[e] = s;
     }
     return 0;
 }

@@ -163,3 +163,19 @@ def test_ex_rejects_bad_operands(lib):
     with pytest.raises(ValueError):      # beta != 0 needs C
         oracle.gemm_ex(False, False, 1.0, np.zeros((3, 4), np.float32),
                        np.zeros((4, 2), np.float32), 1.0, None, lib=lib)
+
+
+@pytest.mark.parametrize("transA,transB", PAIRS)
+def test_ex_entries_match_full_result_bitwise(transA, transB, lib):
+    M, N, K = 70, 90, 333
+    opA = synth.uniform_pm1(81, (M, K))
+    opB = synth.uniform_pm1(82, (K, N))
+    C = synth.uniform_pm1(83, (M, N))
+    A, B = _stored(opA, transA), _stored(opB, transB)
+    full, S = oracle.gemm_ex(transA, transB, -0.75, A, B, 1.25, C, lib=lib)
+    rng = np.random.default_rng(1)
+    rows, cols = rng.integers(0, M, 400), rng.integers(0, N, 400)
+    e, s = oracle.gemm_ex_entries(transA, transB, -0.75, A, B, 1.25, C, rows, cols, lib=lib)
+    assert np.array_equal(e, full[rows, cols]) and np.array_equal(s, S[rows, cols])
+    with pytest.raises(IndexError):
+        oracle.gemm_ex_entries(transA, transB, 1.0, A, B, 0.0, None, [M], [0], lib=lib)

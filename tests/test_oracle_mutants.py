@@ -47,15 +47,16 @@ MUTANTS = {
         "const double b = (double)B[k * ldb + j];",
         "const double b = (double)B[(k % (j + 1)) * ldb + j];"),
     # Mistakes in the general form alpha * op(A) * op(B) + beta * C.
-    "ex_drops_beta_term": ("Out[i * ldo + j] = alpha * acc + c;", "Out[i * ldo + j] = alpha * acc;"),
-    "ex_beta_sign": ("Out[i * ldo + j] = alpha * acc + c;", "Out[i * ldo + j] = alpha * acc - c;"),
-    "ex_ignores_alpha": ("Out[i * ldo + j] = alpha * acc + c;", "Out[i * ldo + j] = acc + c;"),
-    "ex_C_stride_ignores_ld": ("beta * (double)C_in[i * ldc_in + j]", "beta * (double)C_in[i * N + j]"),
-    "ex_transA_stride_ignores_ld": ("(transA ? A[k * lda + i] :", "(transA ? A[k * M + i] :"),
+    "ex_drops_beta_term": ("*out = alpha * acc + c;", "*out = alpha * acc;"),
+    "ex_beta_sign": ("*out = alpha * acc + c;", "*out = alpha * acc - c;"),
+    "ex_ignores_alpha": ("*out = alpha * acc + c;", "*out = acc + c;"),
+    "ex_C_row_stride_short": ("beta * (double)C_in[i * ldc_in + j]", "beta * (double)C_in[i * (ldc_in - (ldc_in > 1)) + j]"),
+    "ex_transA_row_stride_short": ("(transA ? A[k * lda + i] :", "(transA ? A[k * (lda - (lda > 1)) + i] :"),
     "ex_transB_neighbour_k": ("B[j * ldb + k] : B[k * ldb + j]", "B[j * ldb + (k + 1) % K] : B[k * ldb + j]"),
-    "ex_transA_ignored": ("(transA ? A[k * lda + i] : A[i * lda + k])",
-                          "(transA ? A[(k % M) * lda + (i % K)] : A[i * lda + k])"),
+    "ex_transA_neighbour_row": ("(transA ? A[k * lda + i] :", "(transA ? A[k * lda + (i + 1) % lda] :"),
     "ex_scale_drops_c": ("absd(alpha) * accabs + absd(c);", "absd(alpha) * accabs;"),
+    "ex_entries_wrong_element": ("ex_element(transA, transB, rows[e], cols[e],",
+                                 "ex_element(transA, transB, rows[e], cols[(e + 1) % n],"),
     "ex_scale_signed_alpha": ("absd(alpha) * accabs + absd(c);", "alpha * accabs + absd(c);"),
 }
 
@@ -86,6 +87,7 @@ def _battery(lib):
     for tA, tB in pins_ex.PAIRS:
         cases.append((pins_ex.test_ex_small_integers_exact, dict(transA=tA, transB=tB)))
         cases.append((pins_ex.test_ex_leading_dimensions_never_read_padding, dict(transA=tA, transB=tB)))
+        cases.append((pins_ex.test_ex_entries_match_full_result_bitwise, dict(transA=tA, transB=tB)))
     cases += [
         (pins_ex.test_ex_beta_zero_never_reads_C, {}),
         (pins_ex.test_ex_alpha_zero_never_reads_A_or_B, {}),
