@@ -1,4 +1,5 @@
-"""FP32 matrix multiply C = A * B on AMD MI355X (gfx950).
+"""FP32 matrix multiply C = A * B, and C = alpha * op(A) * op(B) + beta * C,
+on AMD MI355X (gfx950).
 
 Python binding of the C ABI declared in ``include/sgemm.h``: argument
 marshalling only. Every step of the product runs in the HIP kernels of
@@ -8,6 +9,10 @@ and streams.
 Raw entry points (same names and arguments as the C ABI):
     sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream, variant) -> status
     sgemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, variant) -> status
+    sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+             stream, variant) -> status
+    sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
+                        C, ldc, variant) -> status
     sgemm_status_string(status) -> str
     sgemm_variant_name(variant) -> str | None
     sgemm_best_variant(M, N, K) -> variant
@@ -16,6 +21,7 @@ integer (0 = null stream).
 
 Tensor convenience:
     matmul(A, B, out=None, variant="best") -> C
+    gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best") -> C
 """
 
 from __future__ import annotations
@@ -35,6 +41,11 @@ SGEMM_ERR_VARIANT = -4
 SGEMM_ERR_LAUNCH = -5
 SGEMM_ERR_DEVICE = -6
 SGEMM_ERR_ALIAS = -7
+SGEMM_ERR_OP = -8
+
+# Transpose flags (sgemm_op).
+SGEMM_OP_N = 0
+SGEMM_OP_T = 1
 
 # Variant codes (sgemm_variant).
 SGEMM_BEST = -1
@@ -46,8 +57,8 @@ VARIANTS = {"best": SGEMM_BEST, "naive": SGEMM_NAIVE, "tiled": SGEMM_TILED,
             "regblock": SGEMM_REGBLOCK, "mfma": SGEMM_MFMA}
 
 # Symbols the shared library exports (the functions of include/sgemm.h).
-EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_status_string",
-           "sgemm_variant_name", "sgemm_best_variant")
+EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args",
+           "sgemm_status_string", "sgemm_variant_name", "sgemm_best_variant")
 
 _lib = None
 
@@ -76,6 +87,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm.restype = i
     lib.sgemm_check_args.argtypes = [i, i, i, vp, i, vp, i, vp, i, i]
     lib.sgemm_check_args.restype = i
+    f = ctypes.c_float
+    lib.sgemm_ex.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp, i]
+    lib.sgemm_ex.restype = i
+    lib.sgemm_ex_check_args.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, i]
+    lib.sgemm_ex_check_args.restype = i
     lib.sgemm_status_string.argtypes = [i]
     lib.sgemm_status_string.restype = ctypes.c_char_p
     lib.sgemm_variant_name.argtypes = [i]
@@ -93,6 +109,16 @@ def sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream, variant) -> int:
 
 def sgemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, variant) -> int:
     return load_library().sgemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, variant)
+
+
+def sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant) -> int:
+    return load_library().sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                   stream, variant)
+
+
+def sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant) -> int:
+    return load_library().sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
+                                              C, ldc, variant)
 
 
 def sgemm_status_string(status: int) -> str:
@@ -116,48 +142,82 @@ def _variant_code(variant) -> int:
     return int(variant)
 
 
-def _ld(t) -> int:
-    """Leading dimension of a row-major 2-D tensor (rows one stride apart)."""
+def _storage(t, name):
+    """(transpose flag, leading dimension) under which the C ABI reads the
+    2-D tensor t as its logical matrix: row-major (unit column stride, rows
+    at least a row apart) is read as is; column-major (unit row stride: a
+    transposed view of a row-major tensor) is read as the transpose of its
+    row-major storage. Row-major is preferred when both apply."""
     rows, cols = t.shape
-    if rows > 1:
-        return t.stride(0)
-    return max(cols, 1)
+    s0, s1 = t.stride()
+    if rows == 0 or cols == 0:
+        return SGEMM_OP_N, max(cols, 1)
+    if (cols == 1 or s1 == 1) and (rows == 1 or s0 >= cols):
+        return SGEMM_OP_N, s0 if rows > 1 else cols
+    if (rows == 1 or s0 == 1) and (cols == 1 or s1 >= rows):
+        return SGEMM_OP_T, s1 if cols > 1 else rows
+    raise ValueError(f"{name} must be row-major or column-major (strides {(s0, s1)})")
 
 
-def matmul(A, B, out=None, variant="best"):
-    """C = A @ B for float32 CUDA tensors A (M x K) and B (K x N).
+def _check_tensor(t, name):
+    import torch
 
-    Operands may be row-major views with a row stride larger than the row
-    length (sub-matrices); ``out`` (M x N, same rules) is overwritten. The
-    kernel is enqueued on the current stream of A's device.
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+
+
+def gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best"):
+    """C = alpha * A @ B + beta * C for float32 GPU tensors A (M x K), B (K x N).
+
+    A and B may be row-major or column-major views (a transposed view such
+    as ``X.t()`` is passed to the kernels as a transposed operand, without a
+    copy). C (M x N, row-major, rows possibly padded) is updated in place; it
+    is read only when beta != 0, and allocated when None (then beta must be
+    0). The kernels are enqueued on the current stream of A's device.
     """
     import torch
 
-    for name, t in (("A", A), ("B", B)):
-        if not isinstance(t, torch.Tensor) or t.dim() != 2:
-            raise TypeError(f"{name} must be a 2-D torch.Tensor")
-        if t.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32, got {t.dtype}")
-        if t.device.type != "cuda":
-            raise ValueError(f"{name} must be on a GPU device")
+    _check_tensor(A, "A")
+    _check_tensor(B, "B")
     M, K = A.shape
     K2, N = B.shape
     if K2 != K:
         raise ValueError(f"inner dimensions differ: {tuple(A.shape)} @ {tuple(B.shape)}")
     if B.device != A.device:
         raise ValueError("A and B are on different devices")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    elif (out.dtype != torch.float32 or out.device != A.device
-          or tuple(out.shape) != (M, N)):
-        raise ValueError("out must be a float32 M x N tensor on A's device")
-    for name, t in (("A", A), ("B", B), ("out", out)):
-        if t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1:
-            raise ValueError(f"{name} must be row-major (unit column stride)")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        _check_tensor(C, "C")
+        if C.device != A.device or tuple(C.shape) != (M, N):
+            raise ValueError("C must be an M x N tensor on A's device")
+    ta, lda = _storage(A, "A")
+    tb, ldb = _storage(B, "B")
+    tc, ldc = _storage(C, "C")
+    if tc != SGEMM_OP_N:
+        raise ValueError("C must be row-major (unit column stride)")
     with torch.cuda.device(A.device):
         stream = torch.cuda.current_stream(A.device).cuda_stream
-        rc = sgemm(M, N, K, A.data_ptr() or None, _ld(A), B.data_ptr() or None, _ld(B),
-                   out.data_ptr() or None, _ld(out), stream or None, _variant_code(variant))
+        rc = sgemm_ex(ta, tb, M, N, K, float(alpha), A.data_ptr() or None, lda,
+                      B.data_ptr() or None, ldb, float(beta), C.data_ptr() or None, ldc,
+                      stream or None, _variant_code(variant))
     if rc != SGEMM_OK:
         raise SgemmError(rc)
-    return out
+    return C
+
+
+def matmul(A, B, out=None, variant="best"):
+    """C = A @ B for float32 GPU tensors A (M x K) and B (K x N).
+
+    Operands may be row-major views with a row stride larger than the row
+    length (sub-matrices) or transposed (column-major) views; ``out`` (M x N,
+    row-major) is overwritten. The kernel is enqueued on the current stream
+    of A's device.
+    """
+    return gemm(A, B, out, 1.0, 0.0, variant)

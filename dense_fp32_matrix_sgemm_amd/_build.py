@@ -22,7 +22,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIBDIR, "libsgemm.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["api.hip", "naive.hip", "tiled.hip", "regblock.hip", "mfma.hip"]
+HIP_SOURCES = ["api.hip", "naive.hip", "tiled.hip", "regblock.hip", "scale.hip",
+               "mfma_nn.hip", "mfma_nt.hip", "mfma_tn.hip", "mfma_tt.hip"]
 CXX_SOURCES = ["args.cpp"]
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -34,28 +34,47 @@ int current_gfx950_cus()
     return state > 0 ? state : 0;
 }
 
+hipError_t launch_mfma(const sgemm_impl::Problem &p, hipStream_t s)
+{
+    if (p.ta) return p.tb ? sgemm_impl::launch_mfma_tt(p, s) : sgemm_impl::launch_mfma_tn(p, s);
+    return p.tb ? sgemm_impl::launch_mfma_nt(p, s) : sgemm_impl::launch_mfma_nn(p, s);
+}
+
 }  // namespace
 
-extern "C" int sgemm(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float *C, int ldc,
-                     void *stream, int variant)
+extern "C" int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha, const float *A, int lda,
+                        const float *B, int ldb, float beta, float *C, int ldc, void *stream, int variant)
 {
-    const int rc = sgemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, variant);
+    const int rc = sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant);
     if (rc != SGEMM_OK) return rc;
     if (M == 0 || N == 0) return SGEMM_OK;
+    const bool product = K > 0 && alpha != 0.0f;
+    if (!product && beta == 1.0f) return SGEMM_OK;  // C = 1 * C: nothing to do
     const int cus = current_gfx950_cus();
     if (cus == 0) return SGEMM_ERR_DEVICE;
 
-    const sgemm_impl::Problem p{A, B, C, lda, ldb, ldc, M, N, K, cus};
+    const sgemm_impl::Problem p{A,   B, C, lda, ldb, ldc, M, N, K, cus, transA == SGEMM_OP_T, transB == SGEMM_OP_T,
+                                alpha, beta};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (variant == SGEMM_BEST) variant = sgemm_best_variant(M, N, K);
 
     hipError_t err;
-    switch (variant) {
-    case SGEMM_NAIVE: err = sgemm_impl::launch_naive(p, s); break;
-    case SGEMM_TILED: err = sgemm_impl::launch_tiled(p, s); break;
-    case SGEMM_REGBLOCK: err = sgemm_impl::launch_regblock(p, s); break;
-    case SGEMM_MFMA: err = sgemm_impl::launch_mfma(p, s); break;
-    default: return SGEMM_ERR_VARIANT;
+    if (!product) {
+        err = sgemm_impl::launch_scale(p, s);
+    } else {
+        switch (variant) {
+        case SGEMM_NAIVE: err = sgemm_impl::launch_naive(p, s); break;
+        case SGEMM_TILED: err = sgemm_impl::launch_tiled(p, s); break;
+        case SGEMM_REGBLOCK: err = sgemm_impl::launch_regblock(p, s); break;
+        case SGEMM_MFMA: err = launch_mfma(p, s); break;
+        default: return SGEMM_ERR_VARIANT;
+        }
     }
     return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+extern "C" int sgemm(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float *C, int ldc,
+                     void *stream, int variant)
+{
+    return sgemm_ex(SGEMM_OP_N, SGEMM_OP_N, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, stream, variant);
 }

@@ -27,22 +27,41 @@ bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi 
 
 bool known_variant(int v) { return v >= SGEMM_BEST && v <= SGEMM_MFMA; }
 
+bool known_op(int op) { return op == SGEMM_OP_N || op == SGEMM_OP_T; }
+
+int at_least_1(int x) { return x > 1 ? x : 1; }
+
 }  // namespace
+
+extern "C" int sgemm_ex_check_args(int transA, int transB, int M, int N, int K, float alpha, const float *A,
+                                   int lda, const float *B, int ldb, float beta, const float *C, int ldc,
+                                   int variant)
+{
+    (void)beta;
+    if (!known_op(transA) || !known_op(transB)) return SGEMM_ERR_OP;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
+    // Stored shapes: A is M x K (K x M when transposed), B is K x N (N x K).
+    const bool ta = transA == SGEMM_OP_T, tb = transB == SGEMM_OP_T;
+    const int a_rows = ta ? K : M, a_cols = ta ? M : K;
+    const int b_rows = tb ? N : K, b_cols = tb ? K : N;
+    if (lda < at_least_1(a_cols) || ldb < at_least_1(b_cols) || ldc < at_least_1(N)) return SGEMM_ERR_LD;
+    if (!known_variant(variant)) return SGEMM_ERR_VARIANT;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (C == nullptr) return SGEMM_ERR_NULL;
+    const bool reads_ab = K > 0 && alpha != 0.0f;
+    if (reads_ab) {
+        if (A == nullptr || B == nullptr) return SGEMM_ERR_NULL;
+        const Span c = span_of(C, M, N, ldc);
+        if (overlap(c, span_of(A, a_rows, a_cols, lda)) || overlap(c, span_of(B, b_rows, b_cols, ldb)))
+            return SGEMM_ERR_ALIAS;
+    }
+    return SGEMM_OK;
+}
 
 extern "C" int sgemm_check_args(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
                                 const float *C, int ldc, int variant)
 {
-    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return SGEMM_ERR_LD;
-    if (!known_variant(variant)) return SGEMM_ERR_VARIANT;
-    if (M == 0 || N == 0) return SGEMM_OK;
-    if (C == nullptr) return SGEMM_ERR_NULL;
-    if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_ERR_NULL;
-    if (K > 0) {
-        const Span c = span_of(C, M, N, ldc);
-        if (overlap(c, span_of(A, M, K, lda)) || overlap(c, span_of(B, K, N, ldb))) return SGEMM_ERR_ALIAS;
-    }
-    return SGEMM_OK;
+    return sgemm_ex_check_args(SGEMM_OP_N, SGEMM_OP_N, M, N, K, 1.0f, A, lda, B, ldb, 0.0f, C, ldc, variant);
 }
 
 extern "C" const char *sgemm_status_string(int status)
@@ -56,6 +75,7 @@ extern "C" const char *sgemm_status_string(int status)
     case SGEMM_ERR_LAUNCH: return "kernel launch failed";
     case SGEMM_ERR_DEVICE: return "no usable gfx950 HIP device";
     case SGEMM_ERR_ALIAS: return "C overlaps A or B";
+    case SGEMM_ERR_OP: return "transpose flag is neither SGEMM_OP_N nor SGEMM_OP_T";
     default: return "unknown status";
     }
 }

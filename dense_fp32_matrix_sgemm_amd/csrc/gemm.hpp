@@ -7,8 +7,11 @@
 
 namespace sgemm_impl {
 
-// One product C = A * B, row-major, leading dimensions in elements. Offsets
-// are formed in 64 bits so that any int-sized problem indexes correctly.
+// One product C = alpha * op(A) * op(B) + beta * C, row-major, leading
+// dimensions in elements. op(A) is M x K: A itself (stored M x K) or, with
+// ta, the transpose of A (stored K x M); op(B) is K x N: B (stored K x N) or,
+// with tb, the transpose of B (stored N x K). Offsets are formed in 64 bits
+// so that any int-sized problem indexes correctly.
 struct Problem {
     const float *A;
     const float *B;
@@ -16,24 +19,37 @@ struct Problem {
     std::int64_t lda, ldb, ldc;
     int M, N, K;
     int cus;  // compute units of the device (for the choice of tile size)
+    bool ta, tb;
+    float alpha, beta;  // C is read only when beta != 0
 };
 
 // Each launcher enqueues the variant's kernel(s) on `stream` and returns the
-// launch status; the problem has already been validated and is non-empty
-// (M > 0, N > 0; K may be 0, in which case the kernels store zeros).
+// launch status; the problem has already been validated and has work to do:
+// M > 0, N > 0, K > 0 and alpha != 0 (the other cases only scale C).
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
 hipError_t launch_tiled(const Problem &p, hipStream_t stream);
 hipError_t launch_regblock(const Problem &p, hipStream_t stream);
-hipError_t launch_mfma(const Problem &p, hipStream_t stream);
+hipError_t launch_mfma_nn(const Problem &p, hipStream_t stream);  // one per transpose pair
+hipError_t launch_mfma_nt(const Problem &p, hipStream_t stream);
+hipError_t launch_mfma_tn(const Problem &p, hipStream_t stream);
+hipError_t launch_mfma_tt(const Problem &p, hipStream_t stream);
+// C = beta * C over the M x N window (zeros, without reading C, when beta is
+// 0): the whole product when K == 0 or alpha == 0.
+hipError_t launch_scale(const Problem &p, hipStream_t stream);
+
+// First element of op(A)'s row r (A's column r when transposed) and of
+// op(B)'s column c (B's row c when transposed).
+__host__ __device__ inline const float *a_row_start(const Problem &p, std::int64_t r) { return p.ta ? p.A + r : p.A + r * p.lda; }
+__host__ __device__ inline const float *b_col_start(const Problem &p, std::int64_t c) { return p.tb ? p.B + c * p.ldb : p.B + c; }
 
 // Largest grid extent used along y (row blocks); kernels loop over the rest.
 constexpr unsigned kMaxGridY = 65535;
 
 // Splits a product over a 1-D grid of BM x BN tiles into bands of at most
 // 2^22 tiles each (far inside the grid limit) and calls launch(sub, tiles_m,
-// tiles_n) for each band. A band is itself a product: A and C start at its
-// first row, B and C at its first column. Band edges fall on multiples of BM
-// and BN, so 16-byte alignment of the operands carries over.
+// tiles_n) for each band. A band is itself a product: op(A) and C start at
+// its first row, op(B) and C at its first column. Band edges fall on
+// multiples of BM and BN, so 16-byte alignment of the operands carries over.
 template <int BM, int BN, class Launch>
 hipError_t for_each_band(const Problem &p, Launch &&launch)
 {
@@ -46,10 +62,8 @@ hipError_t for_each_band(const Problem &p, Launch &&launch)
             Problem q = p;
             q.M = int(p.M - r0 < band_tm * BM ? p.M - r0 : band_tm * BM);
             q.N = int(p.N - c0 < band_tn * BN ? p.N - c0 : band_tn * BN);
-            if (p.K > 0) {  // A and B are not read (and may be NULL) when K == 0
-                q.A = p.A + r0 * p.lda;
-                q.B = p.B + c0;
-            }
+            q.A = a_row_start(p, r0);
+            q.B = b_col_start(p, c0);
             q.C = p.C + r0 * p.ldc + c0;
             const int tiles_m = int((q.M + BM - 1) / BM), tiles_n = int((q.N + BN - 1) / BN);
             const hipError_t e = launch(q, tiles_m, tiles_n);

@@ -5,33 +5,45 @@
 // inputs); on gfx950 the FP32 dense contraction itself has a matrix-core
 // instruction, and it is what the tile hierarchy below feeds.
 //
+// The kernels compute C = alpha * op(A) * op(B) + beta * C (the general form
+// of section 07's vendor call); each transpose pair is its own instantiation,
+// built in its own translation unit (mfma_nn.hip, ...).
+//
 // Hierarchy
 //  * work-group: BM x BN tile of C, WAVES_M x WAVES_N waves, K walked in
 //    slabs of BK; slab t+1 is fetched into registers while slab t is
 //    multiplied out of LDS, then written to the other of two LDS buffers
 //    (one barrier per slab);
 //  * wave: WM x WN = (BM / WAVES_M) x (BN / WAVES_N) tile, held as
-//    MI x (NJ * TI) accumulator blocks of 32 x 32 (16 VGPRs each);
+//    (WM / 32) x (WN / 32) accumulator blocks of 32 x 32 (16 VGPRs each);
 //  * instruction: v_mfma_f32_32x32x2_f32, C[32x32] += A[32x2] * B[2x32].
 //    Lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; accumulator
 //    register r of lane l is C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
 //
-// Operand order. The K order inside a slab is free (any order of the terms
-// gives the sum), so it is chosen to make every LDS read wide:
+// Operands. The instruction treats its two operands alike: lane l gives the
+// operand's free index (row of A, column of B) l % 32 and its k index l / 32.
+// So each operand tile is described the same way (struct Operand), by how it
+// is stored: with k contiguous (A as given, or B transposed: "KC") or with the
+// free index contiguous (B as given, or A transposed: "FC"). The tile keeps
+// its storage order in LDS, so global memory is copied to LDS in 16-byte
+// chunks in every case, and the K order inside a slab (free: any order of the
+// terms gives the sum) is chosen to make every LDS read wide:
 //  * within a group of 8 consecutive k, MFMA step s (0..3) gives lane half h
-//    the k index 4h + s. A lane then needs A[i][4h .. 4h+3] for the four steps:
-//    one 16-byte read from the row-major A tile;
-//  * the 32 columns of one MFMA block are interleaved TI-ways: block t of a
-//    column group covers columns TI*c + t, c = 0..31. Lane c then reads the TI
-//    adjacent values B[k][TI*c .. TI*c+TI-1] of the row-major B tile in one
-//    read and feeds element t to block t. In the epilogue the same lane holds
-//    TI adjacent columns of C and stores them with one wide store.
-// A rows in LDS carry 4 words of padding so the 32 rows read by a half-wave at
-// the same k fall in distinct banks; B rows are read as contiguous spans and
-// are not padded.
+//    the k index 4h + s. From a KC tile a lane then reads the four values
+//    X[f][4h .. 4h+3] for the four steps with one 16-byte read;
+//  * from an FC tile the 32 lanes of one block are interleaved TI-ways: block
+//    t of a group covers free indices TI*c + t, c = 0..31, so lane c reads the
+//    TI adjacent values X[k][TI*c .. TI*c+TI-1] in one read and feeds element
+//    t to block t. In the epilogue a lane then holds TI adjacent columns of C
+//    (B as given) and stores them with one wide store.
+// KC rows in LDS carry 4 words of padding so the 32 rows read by a half-wave
+// at the same k fall in distinct banks; FC rows are read as contiguous spans
+// and are not padded.
 //
 // Ragged shapes: tiles and slabs that cross the edge of A, B or C load zeros
 // outside and drop stores outside; interior tiles take the unguarded path.
+#pragma once
+
 #include <type_traits>
 
 #include "gemm.hpp"
@@ -41,28 +53,32 @@ namespace sgemm_impl {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-// Native 4-wide vector: copies of it stay in registers (copies of the HIP
+// Native short vectors: copies of them stay in registers (copies of the HIP
 // float4 struct through pointers become memcpy and can end up in scratch).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int N>
-struct Vec;
+struct VecT;
 template <>
-struct Vec<1> {
+struct VecT<1> {
     using T = float;
 };
 template <>
-struct Vec<2> {
-    using T = float2;
+struct VecT<2> {
+    using T = f32x2;
 };
 template <>
-struct Vec<4> {
-    using T = float4;
+struct VecT<4> {
+    using T = f32x4;
 };
 
 [[maybe_unused]] __device__ __forceinline__ float elem(float v, int) { return v; }
-__device__ __forceinline__ float elem(float2 v, int t) { return t == 0 ? v.x : v.y; }
-__device__ __forceinline__ float elem(float4 v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; }
+template <class V>
+__device__ __forceinline__ float elem(V v, int t)
+{
+    return v[t];
+}
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
 struct MfmaConfig {
@@ -70,49 +86,182 @@ struct MfmaConfig {
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-    static constexpr int MI = WM / 32;
-    static constexpr int TI = WN >= 128 ? 4 : WN / 32;
-    static constexpr int NJ = WN / (32 * TI);
-    static constexpr int kPadA = 4;
-    static constexpr int kPitchA = BK + kPadA;
-    static constexpr int kLdsFloats = 2 * (BM * kPitchA + BK * BN);  // two stages of A and B tiles
-    static constexpr int kChunksA = BM * BK / 4 / kThreads;  // 4-wide chunks per work-item
-    static constexpr int kChunksB = BK * BN / 4 / kThreads;
 #ifndef SGEMM_MFMA_GROUP_M
 #define SGEMM_MFMA_GROUP_M 8
 #endif
     static constexpr int kGroupM = SGEMM_MFMA_GROUP_M;
     // Waves per SIMD the register allocation aims at: one when a wave's
     // accumulators alone fill the 256 AGPRs, more as they shrink.
-    static constexpr int kWavesPerEU = MI * NJ * TI * 16 >= 256 ? 1 : MI * NJ * TI * 16 >= 64 ? 2 : 4;
+    static constexpr int kAccRegs = (WM / 32) * (WN / 32) * 16;
+    static constexpr int kWavesPerEU = kAccRegs >= 256 ? 1 : kAccRegs >= 64 ? 2 : 4;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(TI == 1 || TI == 2 || TI == 4, "column interleave must be 1, 2 or 4");
-    static_assert(WN == 32 * TI * NJ, "wave tile width must split into interleaved groups");
     static_assert(BK % 8 == 0, "slab depth must be whole groups of 8");
-    static_assert(kChunksA * 4 * kThreads == BM * BK && kChunksB * 4 * kThreads == BK * BN,
-                  "tiles must split evenly over the work-items");
-    static constexpr std::size_t kLdsBytes = sizeof(float) * 2 * (BM * kPitchA + BK * BN);
+};
+
+// One operand's share of a work-group tile: F free indices (rows of op(A)'s
+// tile, or columns of op(B)'s) by BK values of k, of which each wave
+// multiplies W free indices, copied by NT work-items. KC: stored with k
+// contiguous; otherwise with the free index contiguous. In LDS (one stage):
+//   KC: F rows of BK values, padded by 4 words: lds[f * (BK + 4) + k];
+//   FC: BK rows of F values:                    lds[k * F + f].
+// A "stored row" is a row of the operand as it lies in memory: a free index
+// (KC) or a k (FC).
+template <int F, int W, int BK, int NT, bool KC_>
+struct Operand {
+    static constexpr bool KC = KC_;
+    static constexpr int NB = W / 32;                          // MFMA blocks per wave
+    static constexpr int TI = KC ? 1 : (W >= 128 ? 4 : W / 32);  // blocks fed by one LDS read
+    static constexpr int NJ = NB / TI;                         // LDS reads per step (FC)
+    static constexpr int kPitch = KC ? BK + 4 : F;             // LDS row pitch, floats
+    static constexpr int kFloats = KC ? F * (BK + 4) : BK * F;
+    static constexpr int kRows = KC ? F : BK;                  // stored rows in a tile
+    static constexpr int kRowLen = KC ? BK : F;                // stored row length in a tile
+    static constexpr int kRowChunks = kRowLen / 4;             // 16-byte chunks per stored row
+    static constexpr int kChunks = F * BK / 4 / NT;            // chunks per work-item per slab
+    static constexpr int kRowStep = NT / kRowChunks;           // stored rows between them
+    static constexpr int kReads = KC ? NB : 4 * NJ;            // LDS reads per group of 8 k
+    using V = typename VecT<TI>::T;
+    static_assert(TI == 1 || TI == 2 || TI == 4, "interleave must be 1, 2 or 4");
+    static_assert(NB == NJ * TI, "wave tile must split into interleaved groups");
+    static_assert(kChunks * 4 * NT == F * BK, "tile must split evenly over the work-items");
+    static_assert(NT % kRowChunks == 0, "chunk rows must advance evenly");
+
+    // Free index, within the wave's W, of lane column c (0..31) of block b.
+    __device__ static constexpr int free_index(int b, int c)
+    {
+        return KC ? b * 32 + c : (b / TI) * (32 * TI) + c * TI + b % TI;
+    }
+
+    // Operand values of one group of 8 k: element (b, s) feeds block b at
+    // MFMA step s.
+    struct Frag {
+        f32x4 kc[KC ? NB : 1];
+        V fc[4][KC ? 1 : NJ];
+        __device__ float get(int b, int s) const
+        {
+            if constexpr (KC)
+                return kc[b][s];
+            else
+                return elem(fc[s][b / TI], b % TI);
+        }
+    };
+
+    // Fragments of group g of the stage at `lds` for the wave whose free
+    // indices start at w0 (lane column l32, lane half h).
+    __device__ static void read(Frag &fr, const float *lds, int w0, int g, int l32, int h)
+    {
+        if constexpr (KC) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                fr.kc[b] = *reinterpret_cast<const f32x4 *>(&lds[(w0 + b * 32 + l32) * kPitch + 8 * g + 4 * h]);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    fr.fc[s][j] =
+                        *reinterpret_cast<const V *>(&lds[(8 * g + 4 * h + s) * F + w0 + j * 32 * TI + l32 * TI]);
+        }
+    }
+
+    // Chunk c of a slab: stored row and column inside the tile, and its LDS
+    // offset.
+    __device__ static constexpr int chunk_row(int c) { return c / kRowChunks; }
+    __device__ static constexpr int chunk_col(int c) { return (c % kRowChunks) * 4; }
+    __device__ static constexpr int chunk_lds(int c) { return chunk_row(c) * kPitch + chunk_col(c); }
+
+    // Global (stored row, column) of tile element (r, c) of the slab at k0,
+    // for the tile whose free indices start at f0.
+    __device__ static std::int64_t global_row(std::int64_t f0, int k0, int r) { return KC ? f0 + r : k0 + r; }
+    __device__ static int global_col(std::int64_t f0, int k0, int c) { return KC ? k0 + c : int(f0) + c; }
+};
+
+// Operand tiles of one configuration and transpose pair: A is KC unless
+// transposed, B is KC only when transposed.
+template <class Cfg, bool TA, bool TB>
+struct Tiles {
+    using OpA = Operand<Cfg::BM, Cfg::WM, Cfg::BK, Cfg::kThreads, !TA>;
+    using OpB = Operand<Cfg::BN, Cfg::WN, Cfg::BK, Cfg::kThreads, TB>;
+    static constexpr int kLdsFloats = 2 * (OpA::kFloats + OpB::kFloats);  // two stages
+};
+
+// Memory a stored operand is read from: base, leading dimension, and the
+// extent of its free index (M for A, N for B).
+struct OperandRef {
+    const float *X;
+    std::int64_t ld;
+    std::int64_t free_extent;
 };
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
 
+// Zero accumulators.
+template <int NA, int NB>
+__device__ __forceinline__ void clear(floatx16 (&acc)[NA][NB])
+{
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[a][b] = floatx16{};
+}
+
+// The four MFMA steps of one group of 8 k.
+template <class OpA, class OpB>
+__device__ __forceinline__ void mfma_group(floatx16 (&acc)[OpA::NB][OpB::NB], const typename OpA::Frag &fa,
+                                           const typename OpB::Frag &fb)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int a = 0; a < OpA::NB; ++a)
+#pragma unroll
+            for (int b = 0; b < OpB::NB; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.get(a, s), fb.get(b, s), acc[a][b], 0, 0, 0);
+}
+
+// Epilogue: C <- alpha * acc + beta * C for the wave's blocks. Register r of
+// block (a, b) is row OpA::free_index(a, 8(r/4) + 4h + r%4) and column
+// OpB::free_index(b, l32) of the wave tile; the TI blocks of one FC group of
+// B give a lane TI adjacent columns, updated with one access.
+template <class OpA, class OpB>
+__device__ __forceinline__ void write_tile(const Problem &p, const floatx16 (&acc)[OpA::NB][OpB::NB],
+                                           std::int64_t r0, int c0, int l32, int h, bool inside)
+{
+    constexpr int TB = OpB::TI;
+#pragma unroll
+    for (int a = 0; a < OpA::NB; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const std::int64_t row = r0 + OpA::free_index(a, 8 * (r / 4) + 4 * h + (r % 4));
+#pragma unroll
+            for (int j = 0; j < OpB::NJ; ++j) {
+                const int col = c0 + j * 32 * TB + l32 * TB;
+                float v[TB];
+#pragma unroll
+                for (int t = 0; t < TB; ++t) v[t] = acc[a][j * TB + t][r];
+                update_n<TB>(p.C, p.ldc, row, col, p.M, p.N, v, inside, p.alpha, p.beta);
+            }
+        }
+}
+
 // One BM x BN tile (tm, tn) of the product p, with guards on every edge;
-// `lds` holds Cfg::kLdsFloats floats.
-template <class Cfg, bool VEC>
+// `lds` holds Tiles<Cfg, TA, TB>::kLdsFloats floats.
+template <class Cfg, bool TA, bool TB, bool VEC>
 __device__ __forceinline__ void general_tile(const Problem &p, int tm, int tn, float *lds)
 {
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
-    constexpr int MI = Cfg::MI, NJ = Cfg::NJ, TI = Cfg::TI;
-    constexpr int PA = Cfg::kPitchA;
+    using T = Tiles<Cfg, TA, TB>;
+    using OpA = typename T::OpA;
+    using OpB = typename T::OpB;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::kThreads;
     constexpr int G = BK / 8;  // groups of 8 k per slab
-    using VecB = typename Vec<TI>::T;
 
-    float(*As)[BM * PA] = reinterpret_cast<float(*)[BM * PA]>(lds);
-    float(*Bs)[BK * BN] = reinterpret_cast<float(*)[BK * BN]>(lds + 2 * BM * PA);
+    float(*As)[OpA::kFloats] = reinterpret_cast<float(*)[OpA::kFloats]>(lds);
+    float(*Bs)[OpB::kFloats] = reinterpret_cast<float(*)[OpB::kFloats]>(lds + 2 * OpA::kFloats);
 
     const std::int64_t m0 = std::int64_t(tm) * BM;
     const int n0 = tn * BN;
+    const OperandRef ra_{p.A, p.lda, p.M}, rb_{p.B, p.ldb, p.N};
 
     const int tid = threadIdx.x;
     const int lane = tid % 64;
@@ -130,96 +279,61 @@ __device__ __forceinline__ void general_tile(const Problem &p, int tm, int tn, f
     const int n_slabs = (p.K + BK - 1) / BK;
     const int n_full = p.K / BK;
 
-    floatx16 acc[MI][NJ][TI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
-#pragma unroll
-            for (int t = 0; t < TI; ++t) acc[mi][nj][t] = floatx16{};
+    floatx16 acc[OpA::NB][OpB::NB];
+    clear(acc);
 
-    // Global -> register staging of one slab: chunk c of the A tile is row
-    // c / (BK/4), columns 4 (c % (BK/4)) ..; chunk c of the B tile is row
-    // c / (BN/4), columns 4 (c % (BN/4)) ...
-    float4 ra[Cfg::kChunksA], rb[Cfg::kChunksB];
-    auto fetch = [&](int slab, auto guarded) {
-        const int k0 = slab * BK;
+    // Global -> register staging of one slab: chunk c of an operand tile is
+    // stored row chunk_row(c), columns chunk_col(c) .. +3.
+    float4 ra[OpA::kChunks], rb[OpB::kChunks];
+    auto fetch_op = [&](auto op, const OperandRef &x, std::int64_t f0, int k0, float4 *r, auto guarded) {
+        using Op = decltype(op);
 #pragma unroll
-        for (int q = 0; q < Cfg::kChunksA; ++q) {
-            const int c = tid + q * Cfg::kThreads;
-            const std::int64_t row = m0 + c / (BK / 4);
-            const int col = k0 + (c % (BK / 4)) * 4;
-            if constexpr (decltype(guarded)::value)
-                ra[q] = load4_clamped(p.A, p.lda, row, col, p.M, p.K);
-            else
-                ra[q] = load4_inside<VEC>(p.A, p.lda, row, col);
-        }
-#pragma unroll
-        for (int q = 0; q < Cfg::kChunksB; ++q) {
-            const int c = tid + q * Cfg::kThreads;
-            const std::int64_t row = k0 + c / (BN / 4);
-            const int col = n0 + (c % (BN / 4)) * 4;
-            if constexpr (decltype(guarded)::value)
-                rb[q] = load4_clamped(p.B, p.ldb, row, col, p.K, p.N);
-            else
-                rb[q] = load4_inside<VEC>(p.B, p.ldb, row, col);
+        for (int q = 0; q < Op::kChunks; ++q) {
+            const int c = tid + q * NT;
+            const std::int64_t row = Op::global_row(f0, k0, Op::chunk_row(c));
+            const int col = Op::global_col(f0, k0, Op::chunk_col(c));
+            if constexpr (decltype(guarded)::value) {
+                const std::int64_t rows = Op::KC ? x.free_extent : p.K;
+                const int cols = Op::KC ? p.K : int(x.free_extent);
+                r[q] = load4_clamped(x.X, x.ld, row, col, rows, cols);
+            } else {
+                r[q] = load4_inside<VEC>(x.X, x.ld, row, col);
+            }
         }
     };
+    auto stash_op = [&](auto op, const OperandRef &x, std::int64_t f0, int k0, float4 *r, float *dst,
+                        auto guarded) {
+        using Op = decltype(op);
+#pragma unroll
+        for (int q = 0; q < Op::kChunks; ++q) {
+            const int c = tid + q * NT;
+            if constexpr (decltype(guarded)::value) {
+                const std::int64_t rows = Op::KC ? x.free_extent : p.K;
+                const int cols = Op::KC ? p.K : int(x.free_extent);
+                zero_outside(r[q], Op::global_row(f0, k0, Op::chunk_row(c)), Op::global_col(f0, k0, Op::chunk_col(c)),
+                             rows, cols);
+            }
+            *reinterpret_cast<float4 *>(&dst[Op::chunk_lds(c)]) = r[q];
+        }
+    };
+    auto fetch = [&](int slab, auto guarded) {
+        fetch_op(OpA{}, ra_, m0, slab * BK, ra, guarded);
+        fetch_op(OpB{}, rb_, n0, slab * BK, rb, guarded);
+    };
     auto stash = [&](int buf, int slab, auto guarded) {
-        if constexpr (decltype(guarded)::value) {
-            const int k0 = slab * BK;
-#pragma unroll
-            for (int q = 0; q < Cfg::kChunksA; ++q) {
-                const int c = tid + q * Cfg::kThreads;
-                zero_outside(ra[q], m0 + c / (BK / 4), k0 + (c % (BK / 4)) * 4, p.M, p.K);
-            }
-#pragma unroll
-            for (int q = 0; q < Cfg::kChunksB; ++q) {
-                const int c = tid + q * Cfg::kThreads;
-                zero_outside(rb[q], k0 + c / (BN / 4), n0 + (c % (BN / 4)) * 4, p.K, p.N);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < Cfg::kChunksA; ++q) {
-            const int c = tid + q * Cfg::kThreads;
-            *reinterpret_cast<float4 *>(&As[buf][(c / (BK / 4)) * PA + (c % (BK / 4)) * 4]) = ra[q];
-        }
-#pragma unroll
-        for (int q = 0; q < Cfg::kChunksB; ++q) {
-            const int c = tid + q * Cfg::kThreads;
-            *reinterpret_cast<float4 *>(&Bs[buf][(c / (BN / 4)) * BN + (c % (BN / 4)) * 4]) = rb[q];
-        }
+        stash_op(OpA{}, ra_, m0, slab * BK, ra, As[buf], guarded);
+        stash_op(OpB{}, rb_, n0, slab * BK, rb, Bs[buf], guarded);
     };
 
     // Operand fragments of one group of 8 k, double-buffered in registers so
     // the reads of group g+1 are in flight while group g's MFMAs issue.
-    float4 af[2][MI];
-    VecB bf[2][4][NJ];
+    typename OpA::Frag fa[2];
+    typename OpB::Frag fb[2];
     auto read_frags = [&](int buf, int g, int slot) {
-        const float *as = As[buf];
-        const float *bs = Bs[buf];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            af[slot][mi] = *reinterpret_cast<const float4 *>(&as[(wm0 + mi * 32 + l32) * PA + 8 * g + 4 * h]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int nj = 0; nj < NJ; ++nj)
-                bf[slot][s][nj] =
-                    *reinterpret_cast<const VecB *>(&bs[(8 * g + 4 * h + s) * BN + wn0 + nj * 32 * TI + l32 * TI]);
+        OpA::read(fa[slot], As[buf], wm0, g, l32, h);
+        OpB::read(fb[slot], Bs[buf], wn0, g, l32, h);
     };
-    auto mfmas = [&](int slot) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < NJ; ++nj)
-#pragma unroll
-                    for (int t = 0; t < TI; ++t)
-                        acc[mi][nj][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            elem(af[slot][mi], s), elem(bf[slot][s][nj], t), acc[mi][nj][t], 0, 0, 0);
-    };
+    auto mfmas = [&](int slot) { mfma_group<OpA, OpB>(acc, fa[slot], fb[slot]); };
     // Multiply out one LDS buffer; `between` runs half-way through.
     auto multiply = [&](int buf, auto &&between) {
         read_frags(buf, 0, 0);
@@ -265,21 +379,7 @@ __device__ __forceinline__ void general_tile(const Problem &p, int tm, int tn, f
         pipeline(n_slabs, std::true_type{});
     }
 
-    // Epilogue: register r of block (mi, nj, t) is row 8(r/4) + 4h + r%4 of
-    // the block and column TI*l32 + t of its column group.
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const std::int64_t row = m0 + wm0 + mi * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                const int col = n0 + wn0 + nj * 32 * TI + l32 * TI;
-                float v[TI];
-#pragma unroll
-                for (int t = 0; t < TI; ++t) v[t] = acc[mi][nj][t][r];
-                store_n<VEC, TI>(p.C, p.ldc, row, col, p.M, p.N, v, interior);
-            }
+    write_tile<OpA, OpB>(p, acc, m0 + wm0, n0 + wn0, l32, h, interior);
 }
 
 // Interior tiles: the tile lies wholly inside C and the slab loop carries
@@ -295,19 +395,19 @@ __device__ __forceinline__ void general_tile(const Problem &p, int tm, int tn, f
 //  * the barrier sits before the last group of k of the slab, so the first
 //    fragments of the next slab load while that group is multiplied.
 // interior_tile computes one whole BM x BN tile (tm, tn) of the product p
-// (no edge inside it); `lds` holds Cfg::kLdsFloats floats.
-template <class Cfg>
+// (no edge inside it); `lds` holds Tiles<Cfg, TA, TB>::kLdsFloats floats.
+template <class Cfg, bool TA, bool TB>
 __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, float *lds)
 {
+    using T = Tiles<Cfg, TA, TB>;
+    using OpA = typename T::OpA;
+    using OpB = typename T::OpB;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::kThreads;
-    constexpr int MI = Cfg::MI, NJ = Cfg::NJ, TI = Cfg::TI;
-    constexpr int PA = Cfg::kPitchA;
     constexpr int G = BK / 8;
-    constexpr int CA = Cfg::kChunksA, CB = Cfg::kChunksB;
-    using VecB = typename Vec<TI>::T;
+    constexpr int CA = OpA::kChunks, CB = OpB::kChunks;
 
-    float(*As)[BM * PA] = reinterpret_cast<float(*)[BM * PA]>(lds);
-    float(*Bs)[BK * BN] = reinterpret_cast<float(*)[BK * BN]>(lds + 2 * BM * PA);
+    float(*As)[OpA::kFloats] = reinterpret_cast<float(*)[OpA::kFloats]>(lds);
+    float(*Bs)[OpB::kFloats] = reinterpret_cast<float(*)[OpB::kFloats]>(lds + 2 * OpA::kFloats);
 
     const std::int64_t m0 = std::int64_t(tm) * BM;
     const int n0 = tn * BN;
@@ -320,85 +420,55 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
     const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
     const int n_full = p.K / BK;
 
-    floatx16 acc[MI][NJ][TI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
-#pragma unroll
-            for (int t = 0; t < TI; ++t) acc[mi][nj][t] = floatx16{};
+    floatx16 acc[OpA::NB][OpB::NB];
+    clear(acc);
 
-    // This work-item's chunks: A chunk q is row (q*NT + tid) / (BK/4) of the
-    // tile, columns 4 ((q*NT + tid) % (BK/4)) ..; B chunk q is row
-    // (q*NT + tid) / (BN/4), columns 4 ((q*NT + tid) % (BN/4)) ...
-    const float *ga = p.A + (m0 + tid / (BK / 4)) * p.lda + (tid % (BK / 4)) * 4;
-    const float *gb = p.B + std::int64_t(tid / (BN / 4)) * p.ldb + n0 + (tid % (BN / 4)) * 4;
-    constexpr int kRowStepA = NT / (BK / 4);  // tile rows between consecutive chunks q
-    constexpr int kRowStepB = NT / (BN / 4);
-    static_assert(NT % (BK / 4) == 0 && NT % (BN / 4) == 0, "chunk rows must advance evenly");
+    // This work-item's chunks: chunk q of an operand is stored row
+    // chunk_row(q*NT + tid) of the slab, kRowStep stored rows after chunk
+    // q-1. A slab further along K is BK columns (KC) or BK rows (FC) on.
+    const float *ga = p.A + OpA::global_row(m0, 0, OpA::chunk_row(tid)) * p.lda +
+                      OpA::global_col(m0, 0, OpA::chunk_col(tid));
+    const float *gb = p.B + OpB::global_row(n0, 0, OpB::chunk_row(tid)) * p.ldb +
+                      OpB::global_col(n0, 0, OpB::chunk_col(tid));
+    const std::int64_t slab_a = OpA::KC ? BK : BK * p.lda, slab_b = OpB::KC ? BK : BK * p.ldb;
 
     f32x4 ra[CA], rb[CB];
     auto fetch = [&](int slab) {
-        const std::int64_t ka = std::int64_t(slab) * BK, kb = std::int64_t(slab) * BK * p.ldb;
+        const std::int64_t ka = slab * slab_a, kb = slab * slab_b;
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            ra[q] = load16u(ga + q * kRowStepA * p.lda + ka);
+            ra[q] = load16u(ga + q * OpA::kRowStep * p.lda + ka);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            rb[q] = load16u(gb + q * kRowStepB * p.ldb + kb);
+            rb[q] = load16u(gb + q * OpB::kRowStep * p.ldb + kb);
     };
     auto stash = [&](int buf) {
 #pragma unroll
-        for (int q = 0; q < CA; ++q) {
-            const int c = q * NT + tid;
-            *reinterpret_cast<f32x4 *>(&As[buf][(c / (BK / 4)) * PA + (c % (BK / 4)) * 4]) = ra[q];
-        }
+        for (int q = 0; q < CA; ++q)
+            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = ra[q];
 #pragma unroll
-        for (int q = 0; q < CB; ++q) {
-            const int c = q * NT + tid;
-            *reinterpret_cast<f32x4 *>(&Bs[buf][(c / (BN / 4)) * BN + (c % (BN / 4)) * 4]) = rb[q];
-        }
+        for (int q = 0; q < CB; ++q)
+            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = rb[q];
     };
 
-    float4 af[2][MI];
-    VecB bf[2][4][NJ];
+    typename OpA::Frag fa[2];
+    typename OpB::Frag fb[2];
     auto read_frags = [&](int buf, int g, int slot) {
-        const float *as = As[buf];
-        const float *bs = Bs[buf];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            af[slot][mi] = *reinterpret_cast<const float4 *>(&as[(wm0 + mi * 32 + l32) * PA + 8 * g + 4 * h]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int nj = 0; nj < NJ; ++nj)
-                bf[slot][s][nj] =
-                    *reinterpret_cast<const VecB *>(&bs[(8 * g + 4 * h + s) * BN + wn0 + nj * 32 * TI + l32 * TI]);
+        OpA::read(fa[slot], As[buf], wm0, g, l32, h);
+        OpB::read(fb[slot], Bs[buf], wn0, g, l32, h);
     };
-    auto mfmas = [&](int slot) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < NJ; ++nj)
-#pragma unroll
-                    for (int t = 0; t < TI; ++t)
-                        acc[mi][nj][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            elem(af[slot][mi], s), elem(bf[slot][s][nj], t), acc[mi][nj][t], 0, 0, 0);
-    };
-    auto multiply = [&](int buf, auto &&between) {
+    auto mfmas = [&](int slot) { mfma_group<OpA, OpB>(acc, fa[slot], fb[slot]); };
+    auto multiply = [&](int buf) {
         read_frags(buf, 0, 0);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             if (g + 1 < G) read_frags(buf, g + 1, (g + 1) & 1);
-            if (g == G / 2) between();
             mfmas(g & 1);
         }
     };
 
     static_assert(G % 2 == 0, "the pipelined loop needs an even number of k-groups per slab");
-    constexpr int NR = MI + 4 * NJ;            // fragment reads per group
+    constexpr int NR = OpA::kReads + OpB::kReads;  // fragment reads per group
     // Interleave hints: one memory instruction after each MFMA, so no burst
     // of loads or stores holds back the next MFMA in the wave's in-order issue.
     auto interleave_a = [&] {
@@ -473,40 +543,26 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
         __syncthreads();
     }
     if (n_full * BK < p.K) {
-        // Partial last slab: columns k >= K of A and rows k >= K of B read as
-        // zero. Written straight to LDS one element at a time; this runs once.
+        // Partial last slab: k >= K reads as zero. Written straight to LDS one
+        // element at a time; this runs once.
         const int k0 = n_full * BK;
+        auto partial = [&](auto op, const float *X, std::int64_t ld, std::int64_t f0, float *dst) {
+            using Op = decltype(op);
 #pragma unroll 1
-        for (int e = tid; e < BM * BK; e += NT) {
-            const int r = e / BK, k = e % BK;
-            As[0][r * PA + k] = k0 + k < p.K ? p.A[(m0 + r) * p.lda + k0 + k] : 0.0f;
-        }
-#pragma unroll 1
-        for (int e = tid; e < BK * BN; e += NT) {
-            const int k = e / BN, c = e % BN;
-            Bs[0][k * BN + c] = k0 + k < p.K ? p.B[std::int64_t(k0 + k) * p.ldb + n0 + c] : 0.0f;
-        }
+            for (int e = tid; e < Op::kRows * Op::kRowLen; e += NT) {
+                const int r = e / Op::kRowLen, c = e % Op::kRowLen;
+                const int k = Op::KC ? c : r;
+                dst[r * Op::kPitch + c] =
+                    k0 + k < p.K ? X[Op::global_row(f0, k0, r) * ld + Op::global_col(f0, k0, c)] : 0.0f;
+            }
+        };
+        partial(OpA{}, p.A, p.lda, m0, As[0]);
+        partial(OpB{}, p.B, p.ldb, n0, Bs[0]);
         __syncthreads();
-        multiply(0, [] {});
+        multiply(0);
     }
 
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const std::int64_t row = m0 + wm0 + mi * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                const int col = n0 + wn0 + nj * 32 * TI + l32 * TI;
-                float *c = p.C + row * p.ldc + col;
-                if constexpr (TI == 4) {
-                    store16u(c, f32x4{acc[mi][nj][0][r], acc[mi][nj][1][r], acc[mi][nj][2][r], acc[mi][nj][3][r]});
-                } else if constexpr (TI == 2) {
-                    store8u(c, acc[mi][nj][0][r], acc[mi][nj][1][r]);
-                } else {
-                    c[0] = acc[mi][nj][0][r];
-                }
-            }
+    write_tile<OpA, OpB>(p, acc, m0 + wm0, n0 + wn0, l32, h, true);
 }
 
 #ifndef SGEMM_MFMA_TILE
@@ -528,17 +584,14 @@ using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
 using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
 using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
 
-template <class A, class B>
-constexpr int max_lds() { return A::kLdsFloats > B::kLdsFloats ? A::kLdsFloats : B::kLdsFloats; }
-
 // Products too small for a single interior tile: general tiles only.
-template <class Cfg, bool VEC>
+template <class Cfg, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tiles_m)
 {
-    __shared__ __attribute__((aligned(16))) float lds[Cfg::kLdsFloats];
+    __shared__ __attribute__((aligned(16))) float lds[Tiles<Cfg, TA, TB>::kLdsFloats];
     int tm, tn;
     tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, Cfg::kGroupM, tm, tn);
-    general_tile<Cfg, VEC>(p, tm, tn, lds);
+    general_tile<Cfg, TA, TB, VEC>(p, tm, tn, lds);
 }
 
 // Work-group layout of one fused launch: first the interior tiles (whole
@@ -552,23 +605,27 @@ struct FusedGrid {
     int mi, ni;
 };
 
+template <int A, int B>
+constexpr int max_of() { return A > B ? A : B; }
+template <int A, int B>
+constexpr int min_of() { return A < B ? A : B; }
+
 // One launch for the whole product, so the small strips run beside the
 // interior tiles instead of after them; the two bodies share one LDS buffer.
-template <class A, class B>
-constexpr int min_waves() { return A::kWavesPerEU < B::kWavesPerEU ? A::kWavesPerEU : B::kWavesPerEU; }
-
-template <class ICfg, class GCfg, bool VEC>
+template <class ICfg, class GCfg, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(ICfg::kThreads)
-__attribute__((amdgpu_waves_per_eu(min_waves<ICfg, GCfg>(), min_waves<ICfg, GCfg>()))) void mfma_fused_kernel(
-    Problem p, FusedGrid g)
+__attribute__((amdgpu_waves_per_eu(min_of<ICfg::kWavesPerEU, GCfg::kWavesPerEU>(),
+                                   min_of<ICfg::kWavesPerEU, GCfg::kWavesPerEU>()))) void mfma_fused_kernel(Problem p,
+                                                                                                         FusedGrid g)
 {
     static_assert(ICfg::kThreads == GCfg::kThreads, "both bodies run in the same work-group shape");
-    __shared__ __attribute__((aligned(16))) float lds[max_lds<ICfg, GCfg>()];
+    __shared__ __attribute__((aligned(16)))
+    float lds[max_of<Tiles<ICfg, TA, TB>::kLdsFloats, Tiles<GCfg, TA, TB>::kLdsFloats>()];
     const unsigned w = blockIdx.x;
     if (w < g.n_interior) {
         int tm, tn;
         tile_of_workgroup(w, g.n_interior, g.tiles_m, ICfg::kGroupM, tm, tn);
-        interior_tile<ICfg>(p, tm, tn, lds);
+        interior_tile<ICfg, TA, TB>(p, tm, tn, lds);
         return;
     }
     unsigned e = w - g.n_interior;
@@ -576,7 +633,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves<ICfg, GCfg>(), min_waves<ICfg, GCfg
     int tm, tn;
     if (e < g.n_bottom) {
         q.M = p.M - g.mi;
-        if (p.K > 0) q.A = p.A + std::int64_t(g.mi) * p.lda;
+        q.A = a_row_start(p, g.mi);
         q.C = p.C + std::int64_t(g.mi) * p.ldc;
         tm = int(e / unsigned(g.bottom_tn));
         tn = int(e % unsigned(g.bottom_tn));
@@ -584,19 +641,19 @@ __attribute__((amdgpu_waves_per_eu(min_waves<ICfg, GCfg>(), min_waves<ICfg, GCfg
         e -= g.n_bottom;
         q.M = g.mi;
         q.N = p.N - g.ni;
-        if (p.K > 0) q.B = p.B + g.ni;
+        q.B = b_col_start(p, g.ni);
         q.C = p.C + g.ni;
         tm = int(e / unsigned(g.right_tn));
         tn = int(e % unsigned(g.right_tn));
     }
-    general_tile<GCfg, VEC>(q, tm, tn, lds);
+    general_tile<GCfg, TA, TB, VEC>(q, tm, tn, lds);
 }
 
-template <class Cfg>
+template <class Cfg, bool TA, bool TB>
 hipError_t launch_general(const Problem &p, hipStream_t stream)
 {
-    const void *kernel = rows_aligned16(p) ? reinterpret_cast<const void *>(&mfma_kernel<Cfg, true>)
-                                           : reinterpret_cast<const void *>(&mfma_kernel<Cfg, false>);
+    const void *kernel = rows_aligned16(p) ? reinterpret_cast<const void *>(&mfma_kernel<Cfg, TA, TB, true>)
+                                           : reinterpret_cast<const void *>(&mfma_kernel<Cfg, TA, TB, false>);
     return for_each_band<Cfg::BM, Cfg::BN>(p, [&](Problem q, int tiles_m, int tiles_n) {
         void *args[] = {&q, &tiles_m};
         return hipLaunchKernel(kernel, dim3(unsigned(tiles_m) * unsigned(tiles_n)), dim3(Cfg::kThreads), args, 0,
@@ -610,12 +667,12 @@ std::int64_t whole_tiles(const Problem &p)
     return std::int64_t(p.M / Cfg::BM) * std::int64_t(p.N / Cfg::BN);
 }
 
-template <class ICfg, class GCfg>
+template <class ICfg, class GCfg, bool TA, bool TB>
 hipError_t launch_fused(const Problem &p, hipStream_t stream)
 {
     return for_each_band<ICfg::BM, ICfg::BN>(p, [&](Problem q, int, int) {
         const int mi = q.M / ICfg::BM * ICfg::BM, ni = q.N / ICfg::BN * ICfg::BN;
-        if (mi == 0 || ni == 0) return launch_general<GeneralCfg>(q, stream);
+        if (mi == 0 || ni == 0) return launch_general<GeneralCfg, TA, TB>(q, stream);
         FusedGrid g;
         g.tiles_m = mi / ICfg::BM;
         g.n_interior = unsigned(g.tiles_m) * unsigned(ni / ICfg::BN);
@@ -625,8 +682,9 @@ hipError_t launch_fused(const Problem &p, hipStream_t stream)
         g.right_tn = (q.N - ni + GCfg::BN - 1) / GCfg::BN;
         g.n_bottom = mi < q.M ? unsigned((q.M - mi + GCfg::BM - 1) / GCfg::BM) * unsigned(g.bottom_tn) : 0u;
         const unsigned n_right = ni < q.N ? unsigned((mi + GCfg::BM - 1) / GCfg::BM) * unsigned(g.right_tn) : 0u;
-        const void *kernel = rows_aligned16(q) ? reinterpret_cast<const void *>(&mfma_fused_kernel<ICfg, GCfg, true>)
-                                               : reinterpret_cast<const void *>(&mfma_fused_kernel<ICfg, GCfg, false>);
+        const void *kernel = rows_aligned16(q)
+                                 ? reinterpret_cast<const void *>(&mfma_fused_kernel<ICfg, GCfg, TA, TB, true>)
+                                 : reinterpret_cast<const void *>(&mfma_fused_kernel<ICfg, GCfg, TA, TB, false>);
         void *args[] = {&q, &g};
         return hipLaunchKernel(kernel, dim3(g.n_interior + g.n_bottom + n_right), dim3(ICfg::kThreads), args, 0,
                                stream);
@@ -639,16 +697,14 @@ hipError_t launch_fused(const Problem &p, hipStream_t stream)
 // to 128x128 and then 64x64 tiles, which trade operand reuse for parallelism.
 // The strips of a 256x256 split use 128x128 general tiles; the smaller
 // splits use general tiles of their own size.
+template <bool TA, bool TB>
 hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
 {
     const std::int64_t fill = p.cus > 0 ? p.cus : 256;
-    if (whole_tiles<BigCfg>(p) >= fill) return launch_fused<BigCfg, GeneralCfg>(p, stream);
-    if (whole_tiles<MidCfg>(p) >= fill) return launch_fused<MidCfg, MidCfg>(p, stream);
-    return launch_fused<SmallCfg, SmallCfg>(p, stream);
+    if (whole_tiles<BigCfg>(p) >= fill) return launch_fused<BigCfg, GeneralCfg, TA, TB>(p, stream);
+    if (whole_tiles<MidCfg>(p) >= fill) return launch_fused<MidCfg, MidCfg, TA, TB>(p, stream);
+    return launch_fused<SmallCfg, SmallCfg, TA, TB>(p, stream);
 }
 
 }  // namespace
-
-hipError_t launch_mfma(const Problem &p, hipStream_t stream) { return launch_by_shape(p, stream); }
-
 }  // namespace sgemm_impl

@@ -1,0 +1,12 @@
+// MFMA kernels for op(A) = A, op(B) = B (one transpose pair per
+// translation unit, so the four build in parallel).
+#include "mfma.hpp"
+
+namespace sgemm_impl {
+
+hipError_t launch_mfma_nn(const Problem &p, hipStream_t stream)
+{
+    return launch_by_shape<false, false>(p, stream);
+}
+
+}  // namespace sgemm_impl

@@ -1,0 +1,12 @@
+// MFMA kernels for op(A) = A, op(B) = B transposed (one transpose pair per
+// translation unit, so the four build in parallel).
+#include "mfma.hpp"
+
+namespace sgemm_impl {
+
+hipError_t launch_mfma_nt(const Problem &p, hipStream_t stream)
+{
+    return launch_by_shape<false, true>(p, stream);
+}
+
+}  // namespace sgemm_impl

@@ -1,0 +1,12 @@
+// MFMA kernels for op(A) = A transposed, op(B) = B transposed (one transpose pair per
+// translation unit, so the four build in parallel).
+#include "mfma.hpp"
+
+namespace sgemm_impl {
+
+hipError_t launch_mfma_tt(const Problem &p, hipStream_t stream)
+{
+    return launch_by_shape<true, true>(p, stream);
+}
+
+}  // namespace sgemm_impl

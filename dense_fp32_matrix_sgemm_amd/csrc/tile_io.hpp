@@ -92,6 +92,52 @@ __device__ __forceinline__ void zero_outside(float4 &v, std::int64_t row, int c,
     v.w = (r && c + 3 < cols) ? v.w : 0.0f;
 }
 
+// The epilogue's update of one element: alpha * acc, plus beta * old when
+// beta != 0 (old, C's value before the call, is read only then).
+__device__ __forceinline__ float axpby(float alpha, float acc, float beta, float old)
+{
+    return __builtin_fmaf(alpha, acc, beta * old);
+}
+
+// C <- alpha * v + beta * C for N (1, 2 or 4) consecutive elements (row, c ..)
+// of C, reading C only when beta != 0. `inside` promises the whole run lies in
+// C; it then moves as one access (any 4-byte aligned address: gfx950 performs
+// unaligned global accesses). Otherwise elements outside rows x cols are
+// skipped.
+template <int N>
+__device__ __forceinline__ void update_n(float *base, std::int64_t ld, std::int64_t row, int c, std::int64_t rows,
+                                         int cols, const float (&v)[N], bool inside, float alpha, float beta)
+{
+    float *p = base + row * ld + c;
+    if (inside) {
+        if constexpr (N == 4) {
+            f32x4u o = {alpha * v[0], alpha * v[1], alpha * v[2], alpha * v[3]};
+            if (beta != 0.0f) {
+                const f32x4u old = load16u(p);
+                o = f32x4u{axpby(alpha, v[0], beta, old[0]), axpby(alpha, v[1], beta, old[1]),
+                           axpby(alpha, v[2], beta, old[2]), axpby(alpha, v[3], beta, old[3])};
+            }
+            store16u(p, o);
+        } else if constexpr (N == 2) {
+            float o[2] = {alpha * v[0], alpha * v[1]};
+            if (beta != 0.0f) {
+                float old[2];
+                __builtin_memcpy(old, p, sizeof(old));
+                o[0] = axpby(alpha, v[0], beta, old[0]);
+                o[1] = axpby(alpha, v[1], beta, old[1]);
+            }
+            store8u(p, o[0], o[1]);
+        } else {
+            p[0] = beta != 0.0f ? axpby(alpha, v[0], beta, p[0]) : alpha * v[0];
+        }
+        return;
+    }
+    if (row >= rows) return;
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        if (c + e < cols) p[e] = beta != 0.0f ? axpby(alpha, v[e], beta, p[e]) : alpha * v[e];
+}
+
 // Store N (1, 2 or 4) consecutive floats v[0..N-1] at (row, c ..) of C.
 // `inside` promises the whole run lies in C; with VEC it is then one store
 // of 4N bytes (alignment as for load4). Otherwise elements outside rows x

@@ -43,8 +43,15 @@ typedef enum sgemm_status {
     SGEMM_ERR_VARIANT = -4,  /* unknown variant code                             */
     SGEMM_ERR_LAUNCH = -5,   /* the HIP launch itself failed (hipGetLastError)   */
     SGEMM_ERR_DEVICE = -6,   /* no usable HIP device, or it is not gfx950        */
-    SGEMM_ERR_ALIAS = -7     /* C's extent overlaps A's or B's                   */
+    SGEMM_ERR_ALIAS = -7,    /* C's extent overlaps A's or B's                   */
+    SGEMM_ERR_OP = -8        /* transpose flag not SGEMM_OP_N or SGEMM_OP_T      */
 } sgemm_status;
+
+/* Transpose flags of sgemm_ex: how an operand is stored. */
+typedef enum sgemm_op {
+    SGEMM_OP_N = 0,  /* as is: op(X) = X                   */
+    SGEMM_OP_T = 1   /* transposed: op(X) = X^T            */
+} sgemm_op;
 
 /* Kernel variants: the ladder from the pages' naive kernel to matrix cores.
  *  NAIVE    one work-item per element of C, operands straight from global
@@ -99,6 +106,53 @@ int sgemm(int M, int N, int K,
           void *stream, int variant);
 
 /*
+ * The general form of the vendor call on "Matrix Multiplication -- Naive to
+ * Tiled", section 07 (which uses alpha = 1, beta = 0 and no transposes):
+ *
+ *     C = alpha * op(A) * op(B) + beta * C
+ *
+ * with op(A) of M x K, op(B) of K x N and C of M x N, all row-major float32
+ * on `stream` (as for sgemm).
+ *
+ * Arguments
+ *   transA         SGEMM_OP_N: A is stored M x K, lda >= max(1, K);
+ *                  SGEMM_OP_T: A is stored K x M (op(A) = A^T), lda >= max(1, M).
+ *   transB         SGEMM_OP_N: B is stored K x N, ldb >= max(1, N);
+ *                  SGEMM_OP_T: B is stored N x K (op(B) = B^T), ldb >= max(1, K).
+ *   M, N, K        sizes of the product; each >= 0.
+ *   alpha, beta    scalars.
+ *   C, ldc         M x N, ldc >= max(1, N); read (when beta != 0) and written.
+ *   stream, variant  as for sgemm; every variant takes every transpose pair.
+ *
+ * Behaviour (the BLAS conventions)
+ *   - Checks, in this order, before any HIP call: transpose flags, sizes,
+ *     leading dimensions, variant, then (only if M > 0 and N > 0) C == NULL,
+ *     and, when A and B are read, NULL A or B and overlap of C with them.
+ *   - M == 0 or N == 0: returns SGEMM_OK without touching the GPU.
+ *   - beta == 0: C is not read (NaN or Inf in C does not propagate).
+ *   - K == 0 or alpha == 0: A and B are not read (and may be NULL, or overlap
+ *     C); C becomes beta * C, and with beta == 1 the call returns SGEMM_OK
+ *     without touching the GPU.
+ *   - Otherwise each element is alpha * s + beta * c (one fused multiply-add
+ *     of alpha and s onto the rounded beta * c; alpha * s alone when beta ==
+ *     0), s being the float32 sum of section 02 formed as for sgemm; the
+ *     result is within 1e-5 * (|alpha| sum_k |op(A)[i][k]| |op(B)[k][j]| +
+ *     |beta c|) + 1e-6 of the exact value.
+ *   - sgemm(M, N, K, A, lda, B, ldb, C, ldc, stream, v) is exactly
+ *     sgemm_ex(SGEMM_OP_N, SGEMM_OP_N, M, N, K, 1, A, lda, B, ldb, 0, C, ldc,
+ *     stream, v).
+ *
+ * Returns SGEMM_OK or a negative sgemm_status.
+ */
+int sgemm_ex(int transA, int transB, int M, int N, int K,
+             float alpha,
+             const float *A, int lda,
+             const float *B, int ldb,
+             float beta,
+             float *C, int ldc,
+             void *stream, int variant);
+
+/*
  * The host-side argument checks of sgemm() alone, with the same codes and in
  * the same order; makes no HIP call and touches no memory. Returns SGEMM_OK
  * when sgemm() would go on to launch (or return early for an empty C).
@@ -108,6 +162,16 @@ int sgemm_check_args(int M, int N, int K,
                      const float *B, int ldb,
                      const float *C, int ldc,
                      int variant);
+
+/* The host-side argument checks of sgemm_ex() alone (same codes, same
+ * order); makes no HIP call and touches no memory. */
+int sgemm_ex_check_args(int transA, int transB, int M, int N, int K,
+                        float alpha,
+                        const float *A, int lda,
+                        const float *B, int ldb,
+                        float beta,
+                        const float *C, int ldc,
+                        int variant);
 
 /* Static English text for a status code ("unknown status" otherwise). */
 const char *sgemm_status_string(int status);

@@ -70,9 +70,11 @@ def _rows_view(x: np.ndarray, rows: int, cols: int):
         raise ValueError("operand smaller than its logical shape")
     if rows == 0 or cols == 0:
         return x.ctypes.data, max(cols, 1)
-    if x.strides[1] != 4 or x.strides[0] % 4:
+    # A stride along a dimension of extent 1 is never used (numpy leaves it
+    # arbitrary in views such as the transpose of a single row).
+    if (cols > 1 and x.strides[1] != 4) or (rows > 1 and (x.strides[0] % 4 or x.strides[0] < 4 * cols)):
         raise ValueError("operand must be row-major with unit column stride")
-    return x.ctypes.data, x.strides[0] // 4
+    return x.ctypes.data, (x.strides[0] // 4 if rows > 1 else max(cols, 1))
 
 
 def gemm(A: np.ndarray, B: np.ndarray, with_abs: bool = False, lib=None):

@@ -52,3 +52,34 @@ def gemm(A: np.ndarray, B: np.ndarray, variant, ld_pad=(0, 0, 0), offset=(0, 0, 
     if return_buffer:
         return C, cbuf.cpu().numpy(), max(ldc, 1), offset[2]
     return C
+
+
+def gemm_ex(transA: bool, transB: bool, alpha: float, A: np.ndarray, B: np.ndarray, beta: float,
+            C0: np.ndarray, variant, ld_pad=(0, 0, 0), offset=(0, 0, 0), stream=None,
+            return_buffer=False, fill=float("nan")):
+    """Run sgemm_ex on copies of the stored operands A, B and the initial C0
+    (M x N); returns the updated C (numpy float32).
+
+    A is stored M x K (K x M when transA), B K x N (N x K when transB). The
+    padding of every buffer holds ``fill`` (NaN: it must never be read), and
+    with ``return_buffer`` the whole backing buffer of C and its (ld, offset)
+    come back too.
+    """
+    M, N = C0.shape
+    K = A.shape[0] if transA else A.shape[1]
+    lda, ldb, ldc = A.shape[1] + ld_pad[0], B.shape[1] + ld_pad[1], N + ld_pad[2]
+    dA, _ = device_matrix(A, lda, offset[0], fill)
+    dB, _ = device_matrix(B, ldb, offset[1], fill)
+    dC, cbuf = device_matrix(C0, ldc, offset[2], fill=SENTINEL)
+    s = stream or torch.cuda.current_stream()
+    rc = sg.sgemm_ex(sg.SGEMM_OP_T if transA else sg.SGEMM_OP_N, sg.SGEMM_OP_T if transB else sg.SGEMM_OP_N,
+                     M, N, K, alpha, dA.data_ptr(), max(lda, 1), dB.data_ptr(), max(ldb, 1), beta,
+                     dC.data_ptr(), max(ldc, 1), s.cuda_stream,
+                     sg.VARIANTS[variant] if isinstance(variant, str) else variant)
+    if rc != sg.SGEMM_OK:
+        raise sg.SgemmError(rc)
+    s.synchronize()
+    C = dC.cpu().numpy()
+    if return_buffer:
+        return C, cbuf.cpu().numpy(), max(ldc, 1), offset[2]
+    return C

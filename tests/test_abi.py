@@ -38,7 +38,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     codes = [sg.SGEMM_OK, sg.SGEMM_ERR_DIM, sg.SGEMM_ERR_LD, sg.SGEMM_ERR_NULL,
-             sg.SGEMM_ERR_VARIANT, sg.SGEMM_ERR_LAUNCH, sg.SGEMM_ERR_DEVICE, sg.SGEMM_ERR_ALIAS]
+             sg.SGEMM_ERR_VARIANT, sg.SGEMM_ERR_LAUNCH, sg.SGEMM_ERR_DEVICE, sg.SGEMM_ERR_ALIAS,
+             sg.SGEMM_ERR_OP]
     texts = [sg.sgemm_status_string(c) for c in codes]
     assert len(set(texts)) == len(texts)
     assert "unknown status" not in texts
@@ -108,6 +109,83 @@ def test_no_device_is_reported_not_crashed(lib):
     assert rc == sg.SGEMM_ERR_DEVICE
 
 
+N_, T_ = sg.SGEMM_OP_N, sg.SGEMM_OP_T
+
+EX_CASES = [
+    # (transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant) -> status
+    ((2, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, 0), sg.SGEMM_ERR_OP),
+    ((N_, -1, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, 0), sg.SGEMM_ERR_OP),
+    ((2, N_, -1, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, 0), sg.SGEMM_ERR_OP),    # flags checked first
+    ((T_, T_, -1, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, 0), sg.SGEMM_ERR_DIM),
+    # Leading dimensions follow the stored shapes.
+    ((T_, N_, 6, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, 0), sg.SGEMM_ERR_LD),     # A^T stored 4 x 6
+    ((T_, N_, 6, 4, 4, 1.0, A, 6, B, 4, 0.0, C, 4, 0), sg.SGEMM_OK),
+    ((N_, N_, 6, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, 0), sg.SGEMM_OK),
+    ((N_, T_, 4, 6, 3, 1.0, A, 3, B, 2, 0.0, C, 6, 0), sg.SGEMM_ERR_LD),     # B^T stored 6 x 3
+    ((N_, T_, 4, 6, 3, 1.0, A, 3, B, 3, 0.0, C, 6, 0), sg.SGEMM_OK),
+    ((N_, N_, 4, 6, 3, 1.0, A, 3, B, 3, 0.0, C, 6, 0), sg.SGEMM_ERR_LD),     # B stored 3 x 6
+    ((T_, T_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 3, 0), sg.SGEMM_ERR_LD),
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, 9), sg.SGEMM_ERR_VARIANT),
+    # alpha == 0 or K == 0: A and B are not read (NULL or overlapping is fine).
+    ((N_, N_, 4, 4, 4, 0.0, None, 4, None, 4, 2.0, C, 4, 0), sg.SGEMM_OK),
+    ((N_, N_, 4, 4, 4, 0.0, A, 4, B, 4, 2.0, A, 4, 0), sg.SGEMM_OK),
+    ((N_, N_, 4, 4, 4, 1.0, None, 4, B, 4, 2.0, C, 4, 0), sg.SGEMM_ERR_NULL),
+    ((N_, N_, 4, 4, 4, 0.0, None, 4, None, 4, 2.0, None, 4, 0), sg.SGEMM_ERR_NULL),
+    # Overlap is measured on the stored extents: A^T stored 8 x 2 spans 16 floats.
+    ((T_, N_, 2, 4, 8, 1.0, A, 2, B, 4, 0.0, A + 4 * 15, 4, 0), sg.SGEMM_ERR_ALIAS),
+    ((T_, N_, 2, 4, 8, 1.0, A, 2, B, 4, 0.0, A + 4 * 16, 4, 0), sg.SGEMM_OK),
+    ((N_, T_, 4, 2, 8, 1.0, A, 8, B, 8, 0.0, B - 4 * 8, 2, 0), sg.SGEMM_OK),      # C ends where B^T starts
+    ((N_, T_, 4, 2, 8, 1.0, A, 8, B, 8, 0.0, B - 4 * 7, 2, 0), sg.SGEMM_ERR_ALIAS),
+]
+
+
+@pytest.mark.parametrize("args,want", EX_CASES)
+def test_ex_check_args(lib, args, want):
+    assert sg.sgemm_ex_check_args(*args) == want
+
+
+@pytest.mark.parametrize("args,want", [c for c in EX_CASES if c[1] != sg.SGEMM_OK])
+def test_ex_rejects_before_touching_the_gpu(lib, args, want):
+    ta, tb, M, N, K, al, pa, lda, pb, ldb, be, pc, ldc, variant = args
+    assert sg.sgemm_ex(ta, tb, M, N, K, al, pa, lda, pb, ldb, be, pc, ldc, None, variant) == want
+
+
+@pytest.mark.parametrize("args,want", CASES)
+def test_plain_checks_are_the_general_checks(lib, args, want):
+    M, N, K, pa, lda, pb, ldb, pc, ldc, variant = args
+    assert sg.sgemm_ex_check_args(N_, N_, M, N, K, 1.0, pa, lda, pb, ldb, 0.0, pc, ldc, variant) == want
+
+
+def test_ex_nothing_to_do_returns_ok_without_gpu(lib):
+    # Empty C, and C = 1 * C (alpha == 0 or K == 0 with beta == 1).
+    assert sg.sgemm_ex(N_, N_, 0, 5, 5, 1.0, None, 5, None, 5, 0.0, None, 5, None, 3) == sg.SGEMM_OK
+    assert sg.sgemm_ex(T_, N_, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, C, 4, None, 3) == sg.SGEMM_OK
+    assert sg.sgemm_ex(N_, T_, 4, 4, 0, 2.0, None, 1, None, 1, 1.0, C, 4, None, 3) == sg.SGEMM_OK
+
+
+def test_ex_no_device_is_reported_not_crashed(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert sg.sgemm_ex(T_, T_, 4, 4, 4, 1.0, A, 4, B, 4, 0.5, C, 4, None, 3) == sg.SGEMM_ERR_DEVICE
+    assert sg.sgemm_ex(N_, N_, 4, 4, 4, 0.0, None, 4, None, 4, 0.0, C, 4, None, 3) == sg.SGEMM_ERR_DEVICE
+
+
+def test_storage_order_of_tensor_views():
+    import torch
+    x = torch.zeros(5, 7)
+    assert sg._storage(x, "x") == (N_, 7)
+    assert sg._storage(x.t(), "x") == (T_, 7)          # 7 x 5 view of 5 x 7 storage
+    assert sg._storage(x[:, :3], "x") == (N_, 7)
+    assert sg._storage(x[:3].t(), "x") == (T_, 7)
+    assert sg._storage(x[:, 1:2].t(), "x") == (T_, 7)  # one row, elements 7 apart
+    assert sg._storage(x[1:2].t(), "x") == (N_, 1)     # one column, elements adjacent
+    with pytest.raises(ValueError):
+        sg._storage(x[:, 0:1].expand(5, 4), "x")
+    with pytest.raises(ValueError):
+        sg._storage(x[::2, ::2], "x")
+
+
 def test_matmul_rejects_bad_tensors():
     import torch
     a = torch.zeros(3, 4)
@@ -119,3 +197,5 @@ def test_matmul_rejects_bad_tensors():
         sg.matmul(torch.zeros(3), torch.zeros(3, 2))
     with pytest.raises(ValueError):
         sg._variant_code("nope")
+    with pytest.raises(ValueError):
+        sg.gemm(a, torch.zeros(4, 2), beta=1.0)    # beta != 0 needs C
