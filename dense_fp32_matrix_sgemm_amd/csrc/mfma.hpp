@@ -566,19 +566,21 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
 }
 
 #ifndef SGEMM_MFMA_TILE
-#define SGEMM_MFMA_TILE 128, 128, 32, 2, 2
+#define SGEMM_MFMA_TILE 128, 128, 32, 2, 4
 #endif
 #ifndef SGEMM_MFMA_BIG_TILE
-#define SGEMM_MFMA_BIG_TILE 256, 256, 16, 2, 2
+#define SGEMM_MFMA_BIG_TILE 256, 256, 16, 4, 2
 #endif
 #ifndef SGEMM_MFMA_MID_TILE
-#define SGEMM_MFMA_MID_TILE 128, 128, 32, 2, 2
+#define SGEMM_MFMA_MID_TILE 128, 128, 32, 2, 4
 #endif
 #ifndef SGEMM_MFMA_SMALL_TILE
 #define SGEMM_MFMA_SMALL_TILE 64, 64, 32, 2, 2
 #endif
 // Tile shapes (BM, BN, BK, WAVES_M, WAVES_N): the general tiles (edges) and
-// three sizes of interior tile.
+// three sizes of interior tile. The 256x256 and 128x128 tiles run eight
+// waves (two per SIMD), so one wave's loads, LDS traffic and barrier waits
+// overlap the other's matrix instructions; the 64x64 tile runs four.
 using GeneralCfg = MfmaConfig<SGEMM_MFMA_TILE>;
 using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
 using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
