@@ -16,6 +16,7 @@ Raw entry points (same names and arguments as the C ABI):
     sgemm_status_string(status) -> str
     sgemm_variant_name(variant) -> str | None
     sgemm_best_variant(M, N, K) -> variant
+    sgemm_mfma_tile(M, N, cus=0) -> (BM, BN)
 Pointers are integers (device addresses); ``stream`` is a hipStream_t as an
 integer (0 = null stream).
 
@@ -58,7 +59,7 @@ VARIANTS = {"best": SGEMM_BEST, "naive": SGEMM_NAIVE, "tiled": SGEMM_TILED,
 
 # Symbols the shared library exports (the functions of include/sgemm.h).
 EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args",
-           "sgemm_status_string", "sgemm_variant_name", "sgemm_best_variant")
+           "sgemm_status_string", "sgemm_variant_name", "sgemm_best_variant", "sgemm_mfma_tile")
 
 _lib = None
 
@@ -98,6 +99,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_variant_name.restype = ctypes.c_char_p
     lib.sgemm_best_variant.argtypes = [i, i, i]
     lib.sgemm_best_variant.restype = i
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.sgemm_mfma_tile.argtypes = [i, i, i, ip, ip]
+    lib.sgemm_mfma_tile.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -132,6 +136,15 @@ def sgemm_variant_name(variant: int):
 
 def sgemm_best_variant(M: int, N: int, K: int) -> int:
     return load_library().sgemm_best_variant(M, N, K)
+
+
+def sgemm_mfma_tile(M: int, N: int, cus: int = 0):
+    """(BM, BN) of the interior tile the MFMA variant uses for M x N."""
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    rc = load_library().sgemm_mfma_tile(M, N, cus, ctypes.byref(bm), ctypes.byref(bn))
+    if rc != SGEMM_OK:
+        raise SgemmError(rc)
+    return bm.value, bn.value
 
 
 def _variant_code(variant) -> int:

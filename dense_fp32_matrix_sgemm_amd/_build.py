@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(LIBDIR, "libsgemm.so")
 ARCH = "gfx950"
 HIP_SOURCES = ["api.hip", "naive.hip", "tiled.hip", "regblock.hip", "scale.hip",
                "mfma_nn.hip", "mfma_nt.hip", "mfma_tn.hip", "mfma_tt.hip"]
-CXX_SOURCES = ["args.cpp"]
+CXX_SOURCES = ["args.cpp", "select.cpp"]
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include "gemm.hpp"
+#include "select.hpp"
 #include "sgemm.h"
 
 namespace {
@@ -53,8 +54,8 @@ extern "C" int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha
     const int cus = current_gfx950_cus();
     if (cus == 0) return SGEMM_ERR_DEVICE;
 
-    const sgemm_impl::Problem p{A,   B, C, lda, ldb, ldc, M, N, K, cus, transA == SGEMM_OP_T, transB == SGEMM_OP_T,
-                                alpha, beta};
+    const sgemm_impl::Problem p{A,     B,    C,   lda, ldb, ldc, M, N, K, cus, transA == SGEMM_OP_T, transB == SGEMM_OP_T,
+                                alpha, beta, sgemm_impl::choose_mfma_tile(M, N, cus)};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (variant == SGEMM_BEST) variant = sgemm_best_variant(M, N, K);
 

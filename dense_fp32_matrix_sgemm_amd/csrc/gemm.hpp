@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "tiles.hpp"
+
 namespace sgemm_impl {
 
 // One product C = alpha * op(A) * op(B) + beta * C, row-major, leading
@@ -21,6 +23,7 @@ struct Problem {
     int cus;  // compute units of the device (for the choice of tile size)
     bool ta, tb;
     float alpha, beta;  // C is read only when beta != 0
+    MfmaTile tile;      // interior tile shape of the matrix-core variant
 };
 
 // Each launcher enqueues the variant's kernel(s) on `stream` and returns the

@@ -40,8 +40,11 @@
 // at the same k fall in distinct banks; FC rows are read as contiguous spans
 // and are not padded.
 //
-// Ragged shapes: tiles and slabs that cross the edge of A, B or C load zeros
-// outside and drop stores outside; interior tiles take the unguarded path.
+// Ragged shapes: one launch covers C with tiles of one shape; the tiles that
+// cross its bottom or right edge run the same loop with their reads clamped
+// into the operands and their stores guarded (interior_tile), and a partial
+// last slab of K reads zeros past K. Products whose row-contiguous operand
+// is under 4 wide use general_tile, which guards every element instead.
 #pragma once
 
 #include <type_traits>
@@ -191,6 +194,68 @@ struct OperandRef {
     const float *X;
     std::int64_t ld;
     std::int64_t free_extent;
+};
+
+// Where one work-item's chunks of an operand tile come from, for the fast
+// tile body: chunk q of every slab starts at chunk(q) + slab offset. With
+// EDGE, addresses are clamped into the operand (see interior_tile) and
+// place() rotates an FC chunk read from a shifted address back into place.
+template <class Op, bool EDGE>
+struct OperandSource {
+    const float *base;
+    std::int64_t ld;
+    std::int64_t off[EDGE && Op::KC ? Op::kChunks : 1];  // per-chunk offsets (clamped KC rows)
+    int shift;                                           // FC: elements the read was moved left
+
+    __device__ OperandSource(const float *X, std::int64_t ld_, std::int64_t f0, std::int64_t extent, int tid)
+        : base(X), ld(ld_), shift(0)
+    {
+        const int r0 = Op::chunk_row(tid), c0 = Op::chunk_col(tid);
+        if constexpr (Op::KC) {  // stored rows are free indices, columns are k
+            if constexpr (EDGE) {
+#pragma unroll
+                for (int q = 0; q < Op::kChunks; ++q) {
+                    const std::int64_t f = f0 + r0 + q * Op::kRowStep;
+                    off[q] = (f < extent ? f : extent - 1) * ld + c0;
+                }
+            } else {
+                off[0] = (f0 + r0) * ld + c0;
+            }
+        } else {  // stored rows are k, columns are free indices
+            std::int64_t f = f0 + c0;
+            if constexpr (EDGE) {
+                const std::int64_t last = extent - 4;  // extent >= 4
+                const std::int64_t fr = f < last ? f : last;
+                const std::int64_t d = f - fr;
+                shift = int(d < 3 ? d : 3);
+                f = fr;
+            }
+            off[0] = std::int64_t(r0) * ld + f;
+        }
+    }
+    __device__ const float *chunk(int q) const
+    {
+        if constexpr (EDGE && Op::KC)
+            return base + off[q];
+        else
+            return base + off[0] + std::int64_t(q) * Op::kRowStep * ld;
+    }
+    // Element e of the chunk is element e + shift of what was read (the
+    // elements past the operand's edge keep junk).
+    __device__ f32x4 place(f32x4 v) const
+    {
+        if constexpr (EDGE && !Op::KC) {
+            const int s = shift;
+            f32x4 r;
+            r[0] = s == 0 ? v[0] : s == 1 ? v[1] : s == 2 ? v[2] : v[3];
+            r[1] = s == 0 ? v[1] : s == 1 ? v[2] : v[3];
+            r[2] = s == 0 ? v[2] : v[3];
+            r[3] = v[3];
+            return r;
+        } else {
+            return v;
+        }
+    }
 };
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
@@ -382,21 +447,34 @@ __device__ __forceinline__ void general_tile(const Problem &p, int tm, int tn, f
     write_tile<OpA, OpB>(p, acc, m0 + wm0, n0 + wn0, l32, h, interior);
 }
 
-// Interior tiles: the tile lies wholly inside C and the slab loop carries
-// no guard at all. Rows need only the 4-byte alignment of any float: global
-// memory moves in 16-byte accesses that gfx950 performs unaligned. The partial
-// last slab (K not a multiple of BK) is loaded once, with guards, after the
-// loop. Same operand order and LDS layout as general_tile; the slab loop is
-// arranged for a single wave per SIMD:
+// The fast tile body. Rows need only the 4-byte alignment of any float:
+// global memory moves in 16-byte accesses that gfx950 performs unaligned. The
+// partial last slab (K not a multiple of BK) is loaded once, with guards,
+// after the loop. Same operand order and LDS layout as general_tile; the slab
+// loop is arranged for few waves per SIMD:
 //  * each steady-state slab is one straight-line block whose LDS stores,
 //    global loads and fragment reads are spread one per MFMA (a burst of
 //    memory instructions would hold back the next MFMA, as a wave issues in
 //    order);
 //  * the barrier sits before the last group of k of the slab, so the first
 //    fragments of the next slab load while that group is multiplied.
-// interior_tile computes one whole BM x BN tile (tm, tn) of the product p
-// (no edge inside it); `lds` holds Tiles<Cfg, TA, TB>::kLdsFloats floats.
-template <class Cfg, bool TA, bool TB>
+//
+// EDGE tiles (crossing the bottom or right edge of C) run the same loop with
+// no guard in it: every address is kept inside the operand instead.
+//  * A chunk whose free index (a KC row) lies past the operand's extent is
+//    read from the last valid row: its values only reach rows or columns of
+//    C that are never stored.
+//  * An FC chunk (4 consecutive free indices) that crosses the edge is read
+//    from the last 4 valid elements of its row, and rotated in registers
+//    when it is stored to LDS so each valid element lands in its place; a
+//    chunk wholly past the edge is read from there too (its values are never
+//    used). This needs the FC free extent >= 4.
+//  * Only k must read as zero outside [0, K), and full slabs never leave it;
+//    the partial slab is loaded element by element as before. Stores are
+//    guarded.
+// interior_tile computes the BM x BN tile (tm, tn) of the product p; `lds`
+// holds Tiles<Cfg, TA, TB>::kLdsFloats floats.
+template <class Cfg, bool TA, bool TB, bool EDGE>
 __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, float *lds)
 {
     using T = Tiles<Cfg, TA, TB>;
@@ -425,11 +503,10 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
 
     // This work-item's chunks: chunk q of an operand is stored row
     // chunk_row(q*NT + tid) of the slab, kRowStep stored rows after chunk
-    // q-1. A slab further along K is BK columns (KC) or BK rows (FC) on.
-    const float *ga = p.A + OpA::global_row(m0, 0, OpA::chunk_row(tid)) * p.lda +
-                      OpA::global_col(m0, 0, OpA::chunk_col(tid));
-    const float *gb = p.B + OpB::global_row(n0, 0, OpB::chunk_row(tid)) * p.ldb +
-                      OpB::global_col(n0, 0, OpB::chunk_col(tid));
+    // q-1, always in the same column. A slab further along K is BK columns
+    // (KC) or BK rows (FC) on.
+    const OperandSource<OpA, EDGE> srca(p.A, p.lda, m0, p.M, tid);
+    const OperandSource<OpB, EDGE> srcb(p.B, p.ldb, n0, p.N, tid);
     const std::int64_t slab_a = OpA::KC ? BK : BK * p.lda, slab_b = OpB::KC ? BK : BK * p.ldb;
 
     f32x4 ra[CA], rb[CB];
@@ -437,18 +514,18 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
         const std::int64_t ka = slab * slab_a, kb = slab * slab_b;
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            ra[q] = load16u(ga + q * OpA::kRowStep * p.lda + ka);
+            ra[q] = load16u(srca.chunk(q) + ka);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            rb[q] = load16u(gb + q * OpB::kRowStep * p.ldb + kb);
+            rb[q] = load16u(srcb.chunk(q) + kb);
     };
     auto stash = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = ra[q];
+            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[q]);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = rb[q];
+            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[q]);
     };
 
     typename OpA::Frag fa[2];
@@ -546,41 +623,31 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
         // Partial last slab: k >= K reads as zero. Written straight to LDS one
         // element at a time; this runs once.
         const int k0 = n_full * BK;
-        auto partial = [&](auto op, const float *X, std::int64_t ld, std::int64_t f0, float *dst) {
+        // Free indices past the operand's extent are clamped into it (their
+        // values are never used), as in the loop.
+        auto partial = [&](auto op, const float *X, std::int64_t ld, std::int64_t f0, std::int64_t extent,
+                           float *dst) {
             using Op = decltype(op);
 #pragma unroll 1
             for (int e = tid; e < Op::kRows * Op::kRowLen; e += NT) {
                 const int r = e / Op::kRowLen, c = e % Op::kRowLen;
                 const int k = Op::KC ? c : r;
-                dst[r * Op::kPitch + c] =
-                    k0 + k < p.K ? X[Op::global_row(f0, k0, r) * ld + Op::global_col(f0, k0, c)] : 0.0f;
+                const std::int64_t f = f0 + (Op::KC ? r : c);
+                const std::int64_t fc = f < extent ? f : extent - 1;
+                const std::int64_t at = Op::KC ? fc * ld + k0 + k : std::int64_t(k0 + k) * ld + fc;
+                dst[r * Op::kPitch + c] = k0 + k < p.K ? X[at] : 0.0f;
             }
         };
-        partial(OpA{}, p.A, p.lda, m0, As[0]);
-        partial(OpB{}, p.B, p.ldb, n0, Bs[0]);
+        partial(OpA{}, p.A, p.lda, m0, p.M, As[0]);
+        partial(OpB{}, p.B, p.ldb, n0, p.N, Bs[0]);
         __syncthreads();
         multiply(0);
     }
 
-    write_tile<OpA, OpB>(p, acc, m0 + wm0, n0 + wn0, l32, h, true);
+    write_tile<OpA, OpB>(p, acc, m0 + wm0, n0 + wn0, l32, h, !EDGE);
 }
 
-#ifndef SGEMM_MFMA_TILE
-#define SGEMM_MFMA_TILE 128, 128, 32, 2, 4
-#endif
-#ifndef SGEMM_MFMA_BIG_TILE
-#define SGEMM_MFMA_BIG_TILE 256, 256, 16, 4, 2
-#endif
-#ifndef SGEMM_MFMA_MID_TILE
-#define SGEMM_MFMA_MID_TILE 128, 128, 32, 2, 4
-#endif
-#ifndef SGEMM_MFMA_SMALL_TILE
-#define SGEMM_MFMA_SMALL_TILE 64, 64, 32, 2, 2
-#endif
-// Tile shapes (BM, BN, BK, WAVES_M, WAVES_N): the general tiles (edges) and
-// three sizes of interior tile. The 256x256 and 128x128 tiles run eight
-// waves (two per SIMD), so one wave's loads, LDS traffic and barrier waits
-// overlap the other's matrix instructions; the 64x64 tile runs four.
+// Tile shapes (tiles.hpp).
 using GeneralCfg = MfmaConfig<SGEMM_MFMA_TILE>;
 using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
 using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
@@ -596,59 +663,20 @@ __global__ __launch_bounds__(Cfg::kThreads) void mfma_kernel(Problem p, int tile
     general_tile<Cfg, TA, TB, VEC>(p, tm, tn, lds);
 }
 
-// Work-group layout of one fused launch: first the interior tiles (whole
-// ICfg tiles covering rows [0, mi) and columns [0, ni)), then the general
-// tiles of the bottom strip (rows [mi, M), all columns) and of the right
-// strip (rows [0, mi), columns [ni, N)).
-struct FusedGrid {
-    unsigned n_interior, n_bottom;
-    int tiles_m;              // interior tile rows
-    int bottom_tn, right_tn;  // general tiles per row of each strip
-    int mi, ni;
-};
-
-template <int A, int B>
-constexpr int max_of() { return A > B ? A : B; }
-template <int A, int B>
-constexpr int min_of() { return A < B ? A : B; }
-
-// One launch for the whole product, so the small strips run beside the
-// interior tiles instead of after them; the two bodies share one LDS buffer.
-template <class ICfg, class GCfg, bool TA, bool TB, bool VEC>
-__global__ __launch_bounds__(ICfg::kThreads)
-__attribute__((amdgpu_waves_per_eu(min_of<ICfg::kWavesPerEU, GCfg::kWavesPerEU>(),
-                                   min_of<ICfg::kWavesPerEU, GCfg::kWavesPerEU>()))) void mfma_fused_kernel(Problem p,
-                                                                                                         FusedGrid g)
+// One launch over all BM x BN tiles of the product: tiles that cross the
+// bottom or right edge of C take the EDGE body of the same loop.
+template <class Cfg, bool TA, bool TB>
+__global__ __launch_bounds__(Cfg::kThreads)
+__attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mfma_tiles_kernel(Problem p, int tiles_m)
 {
-    static_assert(ICfg::kThreads == GCfg::kThreads, "both bodies run in the same work-group shape");
-    __shared__ __attribute__((aligned(16)))
-    float lds[max_of<Tiles<ICfg, TA, TB>::kLdsFloats, Tiles<GCfg, TA, TB>::kLdsFloats>()];
-    const unsigned w = blockIdx.x;
-    if (w < g.n_interior) {
-        int tm, tn;
-        tile_of_workgroup(w, g.n_interior, g.tiles_m, ICfg::kGroupM, tm, tn);
-        interior_tile<ICfg, TA, TB>(p, tm, tn, lds);
-        return;
-    }
-    unsigned e = w - g.n_interior;
-    Problem q = p;
+    __shared__ __attribute__((aligned(16))) float lds[Tiles<Cfg, TA, TB>::kLdsFloats];
     int tm, tn;
-    if (e < g.n_bottom) {
-        q.M = p.M - g.mi;
-        q.A = a_row_start(p, g.mi);
-        q.C = p.C + std::int64_t(g.mi) * p.ldc;
-        tm = int(e / unsigned(g.bottom_tn));
-        tn = int(e % unsigned(g.bottom_tn));
-    } else {
-        e -= g.n_bottom;
-        q.M = g.mi;
-        q.N = p.N - g.ni;
-        q.B = b_col_start(p, g.ni);
-        q.C = p.C + g.ni;
-        tm = int(e / unsigned(g.right_tn));
-        tn = int(e % unsigned(g.right_tn));
-    }
-    general_tile<GCfg, TA, TB, VEC>(q, tm, tn, lds);
+    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, Cfg::kGroupM, tm, tn);
+    const bool edge = std::int64_t(tm + 1) * Cfg::BM > p.M || std::int64_t(tn + 1) * Cfg::BN > p.N;
+    if (edge)
+        interior_tile<Cfg, TA, TB, true>(p, tm, tn, lds);
+    else
+        interior_tile<Cfg, TA, TB, false>(p, tm, tn, lds);
 }
 
 template <class Cfg, bool TA, bool TB>
@@ -663,49 +691,31 @@ hipError_t launch_general(const Problem &p, hipStream_t stream)
     });
 }
 
-template <class Cfg>
-std::int64_t whole_tiles(const Problem &p)
+template <class Cfg, bool TA, bool TB>
+hipError_t launch_tiles(const Problem &p, hipStream_t stream)
 {
-    return std::int64_t(p.M / Cfg::BM) * std::int64_t(p.N / Cfg::BN);
-}
-
-template <class ICfg, class GCfg, bool TA, bool TB>
-hipError_t launch_fused(const Problem &p, hipStream_t stream)
-{
-    return for_each_band<ICfg::BM, ICfg::BN>(p, [&](Problem q, int, int) {
-        const int mi = q.M / ICfg::BM * ICfg::BM, ni = q.N / ICfg::BN * ICfg::BN;
-        if (mi == 0 || ni == 0) return launch_general<GeneralCfg, TA, TB>(q, stream);
-        FusedGrid g;
-        g.tiles_m = mi / ICfg::BM;
-        g.n_interior = unsigned(g.tiles_m) * unsigned(ni / ICfg::BN);
-        g.mi = mi;
-        g.ni = ni;
-        g.bottom_tn = (q.N + GCfg::BN - 1) / GCfg::BN;
-        g.right_tn = (q.N - ni + GCfg::BN - 1) / GCfg::BN;
-        g.n_bottom = mi < q.M ? unsigned((q.M - mi + GCfg::BM - 1) / GCfg::BM) * unsigned(g.bottom_tn) : 0u;
-        const unsigned n_right = ni < q.N ? unsigned((mi + GCfg::BM - 1) / GCfg::BM) * unsigned(g.right_tn) : 0u;
-        const void *kernel = rows_aligned16(q)
-                                 ? reinterpret_cast<const void *>(&mfma_fused_kernel<ICfg, GCfg, TA, TB, true>)
-                                 : reinterpret_cast<const void *>(&mfma_fused_kernel<ICfg, GCfg, TA, TB, false>);
-        void *args[] = {&q, &g};
-        return hipLaunchKernel(kernel, dim3(g.n_interior + g.n_bottom + n_right), dim3(ICfg::kThreads), args, 0,
+    const void *kernel = reinterpret_cast<const void *>(&mfma_tiles_kernel<Cfg, TA, TB>);
+    return for_each_band<Cfg::BM, Cfg::BN>(p, [&](Problem q, int tiles_m, int tiles_n) {
+        void *args[] = {&q, &tiles_m};
+        return hipLaunchKernel(kernel, dim3(unsigned(tiles_m) * unsigned(tiles_n)), dim3(Cfg::kThreads), args, 0,
                                stream);
     });
 }
 
-// Tile size by shape: the largest interior tile whose whole tiles alone
-// give every compute unit at least one work-group (one 256x256 tile per CU
-// already keeps all four SIMDs of the CU busy); smaller products fall back
-// to 128x128 and then 64x64 tiles, which trade operand reuse for parallelism.
-// The strips of a 256x256 split use 128x128 general tiles; the smaller
-// splits use general tiles of their own size.
+// One launch with the tile shape the host chose for this product
+// (select.cpp). The clamped reads of edge tiles need an FC operand (A
+// transposed, B as given) at least 4 wide; narrower products take the
+// general tiles, which guard every element.
 template <bool TA, bool TB>
 hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
 {
-    const std::int64_t fill = p.cus > 0 ? p.cus : 256;
-    if (whole_tiles<BigCfg>(p) >= fill) return launch_fused<BigCfg, GeneralCfg, TA, TB>(p, stream);
-    if (whole_tiles<MidCfg>(p) >= fill) return launch_fused<MidCfg, MidCfg, TA, TB>(p, stream);
-    return launch_fused<SmallCfg, SmallCfg, TA, TB>(p, stream);
+    if ((TA && p.M < 4) || (!TB && p.N < 4)) return launch_general<GeneralCfg, TA, TB>(p, stream);
+    switch (p.tile) {
+    case MfmaTile::Big: return launch_tiles<BigCfg, TA, TB>(p, stream);
+    case MfmaTile::Mid: return launch_tiles<MidCfg, TA, TB>(p, stream);
+    case MfmaTile::Small: break;
+    }
+    return launch_tiles<SmallCfg, TA, TB>(p, stream);
 }
 
 }  // namespace

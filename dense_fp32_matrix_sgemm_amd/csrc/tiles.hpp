@@ -1,0 +1,37 @@
+// Tile shapes of the matrix-core kernels, shared by the kernels (mfma.hpp)
+// and the host-side choice of tile (select.cpp). Each is BM, BN, BK,
+// WAVES_M, WAVES_N: a work-group computes a BM x BN tile of C with
+// WAVES_M x WAVES_N waves, walking K in slabs of BK.
+#pragma once
+
+// General tiles (every element guarded): products whose operand stored with
+// its free index contiguous (B as given, A transposed) is under 4 wide.
+#ifndef SGEMM_MFMA_TILE
+#define SGEMM_MFMA_TILE 128, 128, 32, 2, 4
+#endif
+// Tiles of the fast loop, largest first. The 256x256 and 128x128 tiles run eight
+// waves (two per SIMD), so one wave's loads, LDS traffic and barrier waits
+// overlap the other's matrix instructions; the 64x64 tile runs four.
+#ifndef SGEMM_MFMA_BIG_TILE
+#define SGEMM_MFMA_BIG_TILE 256, 256, 16, 4, 2
+#endif
+#ifndef SGEMM_MFMA_MID_TILE
+#define SGEMM_MFMA_MID_TILE 128, 128, 32, 2, 4
+#endif
+#ifndef SGEMM_MFMA_SMALL_TILE
+#define SGEMM_MFMA_SMALL_TILE 64, 64, 32, 2, 2
+#endif
+
+namespace sgemm_impl {
+
+// Interior tile shape of one matrix-core launch.
+enum class MfmaTile { Big, Mid, Small };
+
+namespace tiles {
+constexpr int kGeneral[] = {SGEMM_MFMA_TILE};
+constexpr int kBig[] = {SGEMM_MFMA_BIG_TILE};
+constexpr int kMid[] = {SGEMM_MFMA_MID_TILE};
+constexpr int kSmall[] = {SGEMM_MFMA_SMALL_TILE};
+}  // namespace tiles
+
+}  // namespace sgemm_impl

@@ -183,6 +183,18 @@ const char *sgemm_variant_name(int variant);
 /* The concrete variant SGEMM_BEST resolves to for an M x N x K product. */
 int sgemm_best_variant(int M, int N, int K);
 
+/*
+ * The interior tile (BM x BN) the MFMA variant uses for an M x N product on
+ * a device with `cus` compute units (cus <= 0: 256, an MI355X); tiles are
+ * tuned per problem as section 07 and exercise 2 of "Matrix Multiplication --
+ * Naive to Tiled" describe. The choice estimates each shape's launch time
+ * from how its work-groups fall into rounds over the compute units and the
+ * throughput measured for that shape, and takes the fastest. Pure host
+ * logic: no HIP call. Returns SGEMM_OK, SGEMM_ERR_DIM (M or N negative) or
+ * SGEMM_ERR_NULL (BM or BN NULL).
+ */
+int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN);
+
 #ifdef __cplusplus
 }
 #endif

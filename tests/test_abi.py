@@ -199,3 +199,25 @@ def test_matmul_rejects_bad_tensors():
         sg._variant_code("nope")
     with pytest.raises(ValueError):
         sg.gemm(a, torch.zeros(4, 2), beta=1.0)    # beta != 0 needs C
+
+
+def test_mfma_tile_choice(lib):
+    # One 256x256 tile per compute unit at 4096^2; 128x128 when 256x256 tiles
+    # would leave most compute units idle (2048^2); 64x64, several resident
+    # per compute unit, for the ragged shape and small products.
+    assert sg.sgemm_mfma_tile(4096, 4096) == (256, 256)
+    assert sg.sgemm_mfma_tile(8192, 8192) == (256, 256)
+    assert sg.sgemm_mfma_tile(2048, 2048) == (128, 128)
+    assert sg.sgemm_mfma_tile(1024, 1024) == (64, 64)
+    assert sg.sgemm_mfma_tile(3001, 2047) == (64, 64)
+    assert sg.sgemm_mfma_tile(128, 128) == (64, 64)
+    # Fewer compute units shift the choice toward larger tiles.
+    assert sg.sgemm_mfma_tile(2048, 2048, cus=64) == (256, 256)
+    assert sg.sgemm_mfma_tile(4096, 4096, cus=0) == sg.sgemm_mfma_tile(4096, 4096, cus=256)
+
+
+def test_mfma_tile_errors(lib):
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    assert lib.sgemm_mfma_tile(-1, 4, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_ERR_DIM
+    assert lib.sgemm_mfma_tile(4, 4, 0, None, ctypes.byref(bn)) == sg.SGEMM_ERR_NULL
+    assert lib.sgemm_mfma_tile(0, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_OK
