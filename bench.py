@@ -44,7 +44,7 @@ PEAK_HBM_GBS = 8000.0
 
 METRIC = "FP32 SGEMM TFLOP/s at 4096^3 on 1 MI355X; % of FP32 peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mfma_sq4096_traffic.json")
-KERNEL_SOURCES = ["mfma.hpp", "mfma_nn.hip", "tile_io.hpp", "gemm.hpp"]
+KERNEL_SOURCES = ["mfma.hpp", "mfma_nn.hip", "tile_io.hpp", "gemm.hpp", "tiles.hpp", "select.cpp"]
 
 
 def flops(M: int, N: int, K: int) -> int:
