@@ -309,7 +309,7 @@ def main(argv=None) -> int:
                         call()
                         torch.cuda.synchronize()
                         same = bool(torch.equal(dC2, plain))
-                    tot, per_g = time_launches(call, 50, 3)
+                    tot, per_g = time_launches(call, 50, 10)
                     kms = sum(per_g) / len(per_g)
                     key = ("t" if ta else "n") + ("t" if tb else "n") + f"_beta{int(beta)}"
                     general[key] = {"kernel_ms_mean": round(kms, 5),
