@@ -195,5 +195,30 @@ def gemm_ex_entries(transA: bool, transB: bool, alpha: float, A: np.ndarray, B: 
     return out, S
 
 
+def lowp_to_float32(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float32 values of 16-bit encodings: the operands of the
+    reduced-precision workload widen to float32 without rounding, after which
+    the product is gemm / gemm_ex of the widened matrices.
+
+    bf16: the encoding is the upper half of a float32 encoding.
+    f16: IEEE 754 binary16, decoded from its fields: sign s, 5-bit exponent e,
+    10-bit fraction f; value (-1)^s * 2^(e-15) * (1 + f/2^10) for 0 < e < 31,
+    (-1)^s * 2^-14 * (f/2^10) for e = 0, infinity or NaN for e = 31.
+    """
+    b = np.asarray(bits).astype(np.uint32)
+    if dtype == "bf16":
+        return np.ascontiguousarray((b << np.uint32(16)).view(np.float32))
+    if dtype == "f16":
+        sign = np.where(b >> np.uint32(15), -1.0, 1.0)
+        e = ((b >> np.uint32(10)) & np.uint32(0x1F)).astype(np.int64)
+        f = (b & np.uint32(0x3FF)).astype(np.float64)
+        normal = np.ldexp(1.0 + f / 1024.0, e - 15)
+        sub = np.ldexp(f / 1024.0, -14)
+        special = np.where(f == 0, np.inf, np.nan)
+        v = np.where(e == 0, sub, np.where(e == 31, special, normal))
+        return np.ascontiguousarray((sign * v).astype(np.float32))
+    raise ValueError(f"unknown 16-bit type {dtype!r}")
+
+
 def num_threads(lib=None) -> int:
     return (lib or load()).oracle_num_threads()

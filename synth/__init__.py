@@ -18,6 +18,9 @@ Value maps (all results are exactly representable in float32):
 * ``uniform01``  -- the top 24 bits u of each draw, value u * 2**-24, in [0, 1).
 * ``uniform_pm1`` -- (u - 2**23) * 2**-23, in [-1, 1).
 * ``small_int``  -- integers in [lo, hi] from the top 32 bits (modulo map).
+* ``lowp_values`` -- values on the coarser grids that bf16 (8 significant
+  bits) or f16 (11) hold exactly, for the reduced-precision workload;
+  ``to_lowp_bits`` gives their 16-bit encodings.
 
 The pages seed a uniform generator (P1 "Naive Implementation": seed 42 and
 rand()/RAND_MAX over [0, 1]; "From 306 ms to 86 ms", "How each kernel was
@@ -74,6 +77,45 @@ def uniform_pm1(seed: int, shape) -> np.ndarray:
     """float32 matrix with i.i.d. entries (u - 2**23) * 2**-23 in [-1, 1)."""
     u = _top24(seed, shape).astype(np.int64) - (1 << 23)
     return (u.astype(np.float64) * 2.0**-23).astype(np.float32)
+
+
+# 16-bit input types of the reduced-precision workload: significant bits of
+# the value grid each can hold exactly (bf16: 8, f16: 11, counting the
+# implicit bit).
+LOWP_BITS = {"bf16": 8, "f16": 11}
+
+
+def lowp_values(seed: int, shape, dtype: str, dist: str = "u01") -> np.ndarray:
+    """float32 matrix of values exactly representable in ``dtype`` ("bf16" or
+    "f16"): with b = LOWP_BITS[dtype] and u the top b bits of each draw,
+    u * 2**-b in [0, 1) ("u01"), or (u - 2**(b-1)) * 2**-(b-1) in [-1, 1)
+    ("pm1"); "int" gives small integers as ``small_int``."""
+    if dist == "int":
+        return small_int(seed, shape)
+    b = LOWP_BITS[dtype]
+    n = int(np.prod(shape, dtype=np.int64))
+    u = (splitmix64(seed, n) >> np.uint64(64 - b)).reshape(shape).astype(np.int64)
+    if dist == "u01":
+        return (u.astype(np.float64) * 2.0**-b).astype(np.float32)
+    return ((u - (1 << (b - 1))).astype(np.float64) * 2.0**-(b - 1)).astype(np.float32)
+
+
+def to_lowp_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The uint16 encodings of float32 values that ``dtype`` holds exactly:
+    bf16 is the upper half of the float32 encoding, f16 is IEEE binary16.
+    Raises ValueError if a value is not exactly representable."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        u = x.view(np.uint32)
+        if (u & np.uint32(0xFFFF)).any():
+            raise ValueError("value not exactly representable in bf16")
+        return (u >> np.uint32(16)).astype(np.uint16)
+    if dtype == "f16":
+        h = x.astype(np.float16)
+        if not np.array_equal(h.astype(np.float32), x, equal_nan=True):
+            raise ValueError("value not exactly representable in f16")
+        return h.view(np.uint16)
+    raise ValueError(f"unknown 16-bit type {dtype!r}")
 
 
 def small_int(seed: int, shape, lo: int = -8, hi: int = 8) -> np.ndarray:
