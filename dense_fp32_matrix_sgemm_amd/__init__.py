@@ -13,6 +13,10 @@ Raw entry points (same names and arguments as the C ABI):
              stream, variant) -> status
     sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
                         C, ldc, variant) -> status
+    sgemm_lp(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+             ldc, stream) -> status      (A, B: bf16 or f16 encodings)
+    sgemm_lp_check_args(dtype, transA, transB, M, N, K, alpha, A, lda, B,
+                        ldb, beta, C, ldc) -> status
     sgemm_status_string(status) -> str
     sgemm_variant_name(variant) -> str | None
     sgemm_best_variant(M, N, K) -> variant
@@ -23,6 +27,7 @@ integer (0 = null stream).
 Tensor convenience:
     matmul(A, B, out=None, variant="best") -> C
     gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best") -> C
+      (A, B float32; or both bfloat16 or both float16, summed in float32)
 """
 
 from __future__ import annotations
@@ -43,6 +48,12 @@ SGEMM_ERR_LAUNCH = -5
 SGEMM_ERR_DEVICE = -6
 SGEMM_ERR_ALIAS = -7
 SGEMM_ERR_OP = -8
+SGEMM_ERR_DTYPE = -9
+
+# 16-bit operand types (sgemm_lp_type).
+SGEMM_LP_BF16 = 1
+SGEMM_LP_F16 = 2
+LP_TYPES = {"bf16": SGEMM_LP_BF16, "f16": SGEMM_LP_F16}
 
 # Transpose flags (sgemm_op).
 SGEMM_OP_N = 0
@@ -58,7 +69,7 @@ VARIANTS = {"best": SGEMM_BEST, "naive": SGEMM_NAIVE, "tiled": SGEMM_TILED,
             "regblock": SGEMM_REGBLOCK, "mfma": SGEMM_MFMA}
 
 # Symbols the shared library exports (the functions of include/sgemm.h).
-EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args",
+EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args", "sgemm_lp", "sgemm_lp_check_args",
            "sgemm_status_string", "sgemm_variant_name", "sgemm_best_variant", "sgemm_mfma_tile")
 
 _lib = None
@@ -93,6 +104,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_ex.restype = i
     lib.sgemm_ex_check_args.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, i]
     lib.sgemm_ex_check_args.restype = i
+    lib.sgemm_lp.argtypes = [i, i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp]
+    lib.sgemm_lp.restype = i
+    lib.sgemm_lp_check_args.argtypes = [i, i, i, i, i, i, f, vp, i, vp, i, f, vp, i]
+    lib.sgemm_lp_check_args.restype = i
     lib.sgemm_status_string.argtypes = [i]
     lib.sgemm_status_string.restype = ctypes.c_char_p
     lib.sgemm_variant_name.argtypes = [i]
@@ -123,6 +138,14 @@ def sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, strea
 def sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant) -> int:
     return load_library().sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
                                               C, ldc, variant)
+
+
+def sgemm_lp(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream) -> int:
+    return load_library().sgemm_lp(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_lp_check_args(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
+    return load_library().sgemm_lp_check_args(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)
 
 
 def sgemm_status_string(status: int) -> str:
@@ -194,6 +217,9 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best"):
     """
     import torch
 
+    lp = {torch.bfloat16: SGEMM_LP_BF16, torch.float16: SGEMM_LP_F16}
+    if isinstance(A, torch.Tensor) and A.dtype in lp:
+        return _gemm_lp(A, B, C, alpha, beta, lp[A.dtype])
     _check_tensor(A, "A")
     _check_tensor(B, "B")
     M, K = A.shape
@@ -220,6 +246,45 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best"):
         rc = sgemm_ex(ta, tb, M, N, K, float(alpha), A.data_ptr() or None, lda,
                       B.data_ptr() or None, ldb, float(beta), C.data_ptr() or None, ldc,
                       stream or None, _variant_code(variant))
+    if rc != SGEMM_OK:
+        raise SgemmError(rc)
+    return C
+
+
+def _gemm_lp(A, B, C, alpha, beta, dtype):
+    """gemm() for bfloat16 / float16 operands: FP32 result and accumulation."""
+    import torch
+
+    for name, t in (("A", A), ("B", B)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise TypeError(f"{name} must be a 2-D torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device")
+    if B.dtype != A.dtype:
+        raise TypeError(f"A and B must have one 16-bit type, got {A.dtype} and {B.dtype}")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} @ {tuple(B.shape)}")
+    if B.device != A.device:
+        raise ValueError("A and B are on different devices")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        _check_tensor(C, "C")
+        if C.device != A.device or tuple(C.shape) != (M, N):
+            raise ValueError("C must be an M x N float32 tensor on A's device")
+    ta, lda = _storage(A, "A")
+    tb, ldb = _storage(B, "B")
+    tc, ldc = _storage(C, "C")
+    if tc != SGEMM_OP_N:
+        raise ValueError("C must be row-major (unit column stride)")
+    with torch.cuda.device(A.device):
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+        rc = sgemm_lp(dtype, ta, tb, M, N, K, float(alpha), A.data_ptr() or None, lda,
+                      B.data_ptr() or None, ldb, float(beta), C.data_ptr() or None, ldc, stream or None)
     if rc != SGEMM_OK:
         raise SgemmError(rc)
     return C

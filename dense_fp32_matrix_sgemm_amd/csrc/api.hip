@@ -74,6 +74,31 @@ extern "C" int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha
     return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
+extern "C" int sgemm_lp(int dtype, int transA, int transB, int M, int N, int K, float alpha, const void *A, int lda,
+                        const void *B, int ldb, float beta, float *C, int ldc, void *stream)
+{
+    const int rc = sgemm_lp_check_args(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    if (rc != SGEMM_OK) return rc;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    const bool product = K > 0 && alpha != 0.0f;
+    if (!product && beta == 1.0f) return SGEMM_OK;
+    const int cus = current_gfx950_cus();
+    if (cus == 0) return SGEMM_ERR_DEVICE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (!product) {
+        const sgemm_impl::Problem p{nullptr, nullptr, C, 1, 1, ldc, M, N, K, cus, false, false, alpha, beta,
+                                    sgemm_impl::MfmaTile::Big};
+        err = sgemm_impl::launch_scale(p, s);
+    } else {
+        const sgemm_impl::LpProblem p{static_cast<const std::uint16_t *>(A), static_cast<const std::uint16_t *>(B),
+                                      C, lda, ldb, ldc, M, N, K, cus, transA == SGEMM_OP_T, transB == SGEMM_OP_T,
+                                      alpha, beta};
+        err = dtype == SGEMM_LP_BF16 ? sgemm_impl::launch_lowp_bf16(p, s) : sgemm_impl::launch_lowp_f16(p, s);
+    }
+    return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
 extern "C" int sgemm(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float *C, int ldc,
                      void *stream, int variant)
 {

@@ -2,6 +2,7 @@
 //
 // Pure C++: no HIP header and no device call, so these entry points work
 // (and are tested, also under the host sanitizers) on a machine without a GPU.
+#include <cstddef>
 #include <cstdint>
 
 #include "sgemm.h"
@@ -14,13 +15,13 @@ struct Span {
     std::uintptr_t lo, hi;
 };
 
-Span span_of(const float *p, int rows, int cols, int ld)
+Span span_of(const void *p, int rows, int cols, int ld, std::size_t elem = sizeof(float))
 {
     const std::uintptr_t base = reinterpret_cast<std::uintptr_t>(p);
     if (rows <= 0 || cols <= 0) return {base, base};
     const std::uint64_t last = static_cast<std::uint64_t>(rows - 1) * static_cast<std::uint64_t>(ld) +
                                static_cast<std::uint64_t>(cols);
-    return {base, base + last * sizeof(float)};
+    return {base, base + last * elem};
 }
 
 bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
@@ -58,6 +59,29 @@ extern "C" int sgemm_ex_check_args(int transA, int transB, int M, int N, int K, 
     return SGEMM_OK;
 }
 
+extern "C" int sgemm_lp_check_args(int dtype, int transA, int transB, int M, int N, int K, float alpha,
+                                   const void *A, int lda, const void *B, int ldb, float beta, const float *C,
+                                   int ldc)
+{
+    (void)beta;
+    if (dtype != SGEMM_LP_BF16 && dtype != SGEMM_LP_F16) return SGEMM_ERR_DTYPE;
+    if (!known_op(transA) || !known_op(transB)) return SGEMM_ERR_OP;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
+    const bool ta = transA == SGEMM_OP_T, tb = transB == SGEMM_OP_T;
+    const int a_rows = ta ? K : M, a_cols = ta ? M : K;
+    const int b_rows = tb ? N : K, b_cols = tb ? K : N;
+    if (lda < at_least_1(a_cols) || ldb < at_least_1(b_cols) || ldc < at_least_1(N)) return SGEMM_ERR_LD;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (C == nullptr) return SGEMM_ERR_NULL;
+    if (K > 0 && alpha != 0.0f) {
+        if (A == nullptr || B == nullptr) return SGEMM_ERR_NULL;
+        const Span c = span_of(C, M, N, ldc);
+        if (overlap(c, span_of(A, a_rows, a_cols, lda, 2)) || overlap(c, span_of(B, b_rows, b_cols, ldb, 2)))
+            return SGEMM_ERR_ALIAS;
+    }
+    return SGEMM_OK;
+}
+
 extern "C" int sgemm_check_args(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
                                 const float *C, int ldc, int variant)
 {
@@ -76,6 +100,7 @@ extern "C" const char *sgemm_status_string(int status)
     case SGEMM_ERR_DEVICE: return "no usable gfx950 HIP device";
     case SGEMM_ERR_ALIAS: return "C overlaps A or B";
     case SGEMM_ERR_OP: return "transpose flag is neither SGEMM_OP_N nor SGEMM_OP_T";
+    case SGEMM_ERR_DTYPE: return "16-bit operand type is neither SGEMM_LP_BF16 nor SGEMM_LP_F16";
     default: return "unknown status";
     }
 }

@@ -45,6 +45,22 @@ hipError_t launch_scale(const Problem &p, hipStream_t stream);
 __host__ __device__ inline const float *a_row_start(const Problem &p, std::int64_t r) { return p.ta ? p.A + r : p.A + r * p.lda; }
 __host__ __device__ inline const float *b_col_start(const Problem &p, std::int64_t c) { return p.tb ? p.B + c * p.ldb : p.B + c; }
 
+// The reduced-precision workload: A and B hold 16-bit encodings (bf16 or
+// f16), products are summed in FP32, C is FP32; otherwise as Problem.
+enum class LpType { BF16, F16 };
+struct LpProblem {
+    const std::uint16_t *A;
+    const std::uint16_t *B;
+    float *C;
+    std::int64_t lda, ldb, ldc;
+    int M, N, K;
+    int cus;
+    bool ta, tb;
+    float alpha, beta;
+};
+hipError_t launch_lowp_bf16(const LpProblem &p, hipStream_t stream);
+hipError_t launch_lowp_f16(const LpProblem &p, hipStream_t stream);
+
 // Largest grid extent used along y (row blocks); kernels loop over the rest.
 constexpr unsigned kMaxGridY = 65535;
 

@@ -1,0 +1,9 @@
+// Reduced-precision kernels with bf16 operands (one dtype per translation
+// unit, so the two build in parallel).
+#include "lowp.hpp"
+
+namespace sgemm_impl {
+
+hipError_t launch_lowp_bf16(const LpProblem &p, hipStream_t stream) { return lp_launch_any<LpType::BF16>(p, stream); }
+
+}  // namespace sgemm_impl

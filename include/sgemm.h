@@ -44,8 +44,15 @@ typedef enum sgemm_status {
     SGEMM_ERR_LAUNCH = -5,   /* the HIP launch itself failed (hipGetLastError)   */
     SGEMM_ERR_DEVICE = -6,   /* no usable HIP device, or it is not gfx950        */
     SGEMM_ERR_ALIAS = -7,    /* C's extent overlaps A's or B's                   */
-    SGEMM_ERR_OP = -8        /* transpose flag not SGEMM_OP_N or SGEMM_OP_T      */
+    SGEMM_ERR_OP = -8,       /* transpose flag not SGEMM_OP_N or SGEMM_OP_T      */
+    SGEMM_ERR_DTYPE = -9     /* 16-bit type not SGEMM_LP_BF16 or SGEMM_LP_F16    */
 } sgemm_status;
+
+/* 16-bit operand types of sgemm_lp. */
+typedef enum sgemm_lp_type {
+    SGEMM_LP_BF16 = 1,  /* bfloat16: the upper 16 bits of an IEEE binary32     */
+    SGEMM_LP_F16 = 2    /* IEEE 754 binary16                                   */
+} sgemm_lp_type;
 
 /* Transpose flags of sgemm_ex: how an operand is stored. */
 typedef enum sgemm_op {
@@ -172,6 +179,44 @@ int sgemm_ex_check_args(int transA, int transB, int M, int N, int K,
                         float beta,
                         const float *C, int ldc,
                         int variant);
+
+/*
+ * The reduced-precision workload: the tensor-core variant "Matrix
+ * Multiplication -- Naive to Tiled", section 07 names (16-bit inputs, FP32
+ * accumulation), in the general form of sgemm_ex:
+ *
+ *     C = alpha * op(A) * op(B) + beta * C
+ *
+ * with A and B holding 16-bit encodings of type `dtype` (SGEMM_LP_BF16 or
+ * SGEMM_LP_F16) and C float32. Every product of two 16-bit values is exact in
+ * float32, and the products are summed in float32 on the matrix cores
+ * (v_mfma_f32_32x32x16_bf16 / _f16), in an order of the kernel's own.
+ *
+ * Arguments are those of sgemm_ex with A and B typed `const void *` (16-bit
+ * elements; leading dimensions in elements; any 2-byte alignment), and no
+ * variant: the matrix-core kernel always runs (a one-work-item-per-element
+ * kernel takes products whose row-contiguous operand is under 8 wide).
+ *
+ * Behaviour: as sgemm_ex (the same checks in the same order, with the type
+ * first: SGEMM_ERR_DTYPE; the same BLAS read rules; C must not overlap A or B
+ * when they are read). Returns SGEMM_OK or a negative sgemm_status.
+ */
+int sgemm_lp(int dtype, int transA, int transB, int M, int N, int K,
+             float alpha,
+             const void *A, int lda,
+             const void *B, int ldb,
+             float beta,
+             float *C, int ldc,
+             void *stream);
+
+/* The host-side argument checks of sgemm_lp() alone (same codes, same
+ * order); makes no HIP call and touches no memory. */
+int sgemm_lp_check_args(int dtype, int transA, int transB, int M, int N, int K,
+                        float alpha,
+                        const void *A, int lda,
+                        const void *B, int ldb,
+                        float beta,
+                        const float *C, int ldc);
 
 /* Static English text for a status code ("unknown status" otherwise). */
 const char *sgemm_status_string(int status);

@@ -83,3 +83,43 @@ def gemm_ex(transA: bool, transB: bool, alpha: float, A: np.ndarray, B: np.ndarr
     if return_buffer:
         return C, cbuf.cpu().numpy(), max(ldc, 1), offset[2]
     return C
+
+
+LP_NAN = 0x7FFF  # a NaN encoding in both bf16 and f16
+
+
+def device_u16(bits: np.ndarray, ld: int | None = None, offset: int = 0, fill: int = LP_NAN):
+    """A rows x cols device view of 16-bit encodings ``bits`` (uint16) with
+    leading dimension ``ld``, starting ``offset`` elements into a buffer whose
+    other elements hold ``fill``. Returns (view, backing buffer)."""
+    rows, cols = bits.shape
+    ld = max(cols, 1) if ld is None else ld
+    buf = torch.full((offset + rows * ld + 8,), np.int16(np.uint16(fill).view(np.int16)).item(), dtype=torch.int16)
+    view = torch.as_strided(buf, (rows, cols), (ld, 1), offset)
+    view.copy_(torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)))
+    dbuf = buf.cuda()
+    return torch.as_strided(dbuf, (rows, cols), (ld, 1), offset), dbuf
+
+
+def gemm_lp(dtype: str, transA: bool, transB: bool, alpha: float, A_bits: np.ndarray, B_bits: np.ndarray,
+            beta: float, C0: np.ndarray, ld_pad=(0, 0, 0), offset=(0, 0, 0), return_buffer=False):
+    """Run sgemm_lp on 16-bit encodings A_bits (stored M x K, or K x M when
+    transA) and B_bits (K x N, or N x K when transB) with the float32 C0;
+    returns the updated C (numpy float32)."""
+    M, N = C0.shape
+    K = A_bits.shape[0] if transA else A_bits.shape[1]
+    lda, ldb, ldc = A_bits.shape[1] + ld_pad[0], B_bits.shape[1] + ld_pad[1], N + ld_pad[2]
+    dA, _ = device_u16(A_bits, lda, offset[0])
+    dB, _ = device_u16(B_bits, ldb, offset[1])
+    dC, cbuf = device_matrix(C0, ldc, offset[2], fill=SENTINEL)
+    s = torch.cuda.current_stream()
+    rc = sg.sgemm_lp(sg.LP_TYPES[dtype], sg.SGEMM_OP_T if transA else sg.SGEMM_OP_N,
+                     sg.SGEMM_OP_T if transB else sg.SGEMM_OP_N, M, N, K, alpha, dA.data_ptr(), max(lda, 1),
+                     dB.data_ptr(), max(ldb, 1), beta, dC.data_ptr(), max(ldc, 1), s.cuda_stream)
+    if rc != sg.SGEMM_OK:
+        raise sg.SgemmError(rc)
+    s.synchronize()
+    C = dC.cpu().numpy()
+    if return_buffer:
+        return C, cbuf.cpu().numpy(), max(ldc, 1), offset[2]
+    return C

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     codes = [sg.SGEMM_OK, sg.SGEMM_ERR_DIM, sg.SGEMM_ERR_LD, sg.SGEMM_ERR_NULL,
              sg.SGEMM_ERR_VARIANT, sg.SGEMM_ERR_LAUNCH, sg.SGEMM_ERR_DEVICE, sg.SGEMM_ERR_ALIAS,
-             sg.SGEMM_ERR_OP]
+             sg.SGEMM_ERR_OP, sg.SGEMM_ERR_DTYPE]
     texts = [sg.sgemm_status_string(c) for c in codes]
     assert len(set(texts)) == len(texts)
     assert "unknown status" not in texts
@@ -221,3 +221,42 @@ def test_mfma_tile_errors(lib):
     assert lib.sgemm_mfma_tile(-1, 4, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_ERR_DIM
     assert lib.sgemm_mfma_tile(4, 4, 0, None, ctypes.byref(bn)) == sg.SGEMM_ERR_NULL
     assert lib.sgemm_mfma_tile(0, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_OK
+
+
+BF, F16 = sg.SGEMM_LP_BF16, sg.SGEMM_LP_F16
+
+LP_CASES = [
+    # (dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc) -> status
+    ((0, N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4), sg.SGEMM_ERR_DTYPE),
+    ((3, 2, N_, -1, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4), sg.SGEMM_ERR_DTYPE),     # type checked first
+    ((BF, 2, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4), sg.SGEMM_ERR_OP),
+    ((F16, N_, N_, 4, -1, 4, 1.0, A, 4, B, 4, 0.0, C, 4), sg.SGEMM_ERR_DIM),
+    ((BF, T_, N_, 6, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4), sg.SGEMM_ERR_LD),      # A^T stored 4 x 6
+    ((BF, T_, N_, 6, 4, 4, 1.0, A, 6, B, 4, 0.0, C, 4), sg.SGEMM_OK),
+    ((F16, N_, T_, 4, 6, 3, 1.0, A, 3, B, 2, 0.0, C, 6), sg.SGEMM_ERR_LD),     # B^T stored 6 x 3
+    ((F16, N_, N_, 0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4), sg.SGEMM_OK),
+    ((BF, N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, None, 4), sg.SGEMM_ERR_NULL),
+    ((BF, N_, N_, 4, 4, 4, 1.0, None, 4, B, 4, 0.0, C, 4), sg.SGEMM_ERR_NULL),
+    ((BF, N_, N_, 4, 4, 4, 0.0, None, 4, None, 4, 2.0, C, 4), sg.SGEMM_OK),    # alpha = 0: A, B unread
+    # Overlap on 2-byte elements: A (4 x 4 bf16) spans 32 bytes.
+    ((BF, N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, A + 30, 4), sg.SGEMM_ERR_ALIAS),
+    ((BF, N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, A + 32, 4), sg.SGEMM_OK),
+]
+
+
+@pytest.mark.parametrize("args,want", LP_CASES)
+def test_lp_check_args(lib, args, want):
+    assert sg.sgemm_lp_check_args(*args) == want
+
+
+@pytest.mark.parametrize("args,want", [c for c in LP_CASES if c[1] != sg.SGEMM_OK])
+def test_lp_rejects_before_touching_the_gpu(lib, args, want):
+    assert sg.sgemm_lp(*args, None) == want
+
+
+def test_lp_no_device_is_reported_not_crashed(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert sg.sgemm_lp(BF, N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, None) == sg.SGEMM_ERR_DEVICE
+    assert sg.sgemm_lp(F16, N_, N_, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, C, 4, None) == sg.SGEMM_OK

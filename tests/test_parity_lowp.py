@@ -1,0 +1,174 @@
+"""Parity of the reduced-precision workload (bf16 / f16 operands, FP32
+accumulation) with the oracle (GPU tests).
+
+The oracle is the general-form oracle applied to the operands widened
+exactly to float32 (oracle.lowp_to_float32). Products of two 16-bit values are
+exact in float32, so the only rounding is the FP32 summation, and the
+acceptance bound is the FP32 path's: |C - Cref| <= 1e-5 * S + 1e-6 with
+S = |alpha| sum_k |op(A)_ik op(B)_kj| + |beta C0_ij|; bit-exact on small
+integers.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dense_fp32_matrix_sgemm_amd as sg
+import oracle
+import synth
+from oracle.check import assert_within
+from tests.gpu_util import SENTINEL, gemm_lp
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(False, False), (False, True), (True, False), (True, True)]
+PAIR_IDS = ["nn", "nt", "tn", "tt"]
+DTYPES = ["bf16", "f16"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sg.load_library()
+
+
+def _stored(x, trans):
+    return np.ascontiguousarray(x.T) if trans else x
+
+
+def _case(dtype, M, N, K, seed, dist="pm1"):
+    """Stored-order-free operands: op(A) values, op(B) values (exact in
+    dtype) and a float32 C0."""
+    return (synth.lowp_values(seed, (M, K), dtype, dist), synth.lowp_values(seed + 1, (K, N), dtype, dist),
+            synth.uniform_pm1(seed + 2, (M, N)))
+
+
+def _run(dtype, tA, tB, alpha, opA, opB, beta, C0, **kw):
+    """(GPU result, oracle result, error scale) for one product."""
+    A = synth.to_lowp_bits(_stored(opA, tA), dtype)
+    B = synth.to_lowp_bits(_stored(opB, tB), dtype)
+    C = gemm_lp(dtype, tA, tB, alpha, A, B, beta, C0, **kw)
+    Cref, S = oracle.gemm_ex(tA, tB, alpha, oracle.lowp_to_float32(A, dtype), oracle.lowp_to_float32(B, dtype),
+                             beta, C0)
+    return C, Cref, S
+
+
+SHAPES = [(1, 1, 1), (5, 3, 7), (8, 8, 8), (17, 15, 17), (33, 31, 7), (65, 63, 65), (129, 127, 129),
+          (255, 257, 33), (300, 1, 129), (1, 300, 129), (256, 256, 255), (520, 776, 336)]
+SCALARS = [(1.0, 0.0), (-1.5, 0.75), (float(np.float32(0.3)), -2.0), (2.0, 1.0)]
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_shapes_and_scalars(dtype, pair):
+    tA, tB = pair
+    print(f"[lowp] shapes {dtype} {pair}", flush=True)
+    for idx, (M, N, K) in enumerate(SHAPES):
+        opA, opB, C0 = _case(dtype, M, N, K, 100 + 10 * idx)
+        alpha, beta = SCALARS[idx % len(SCALARS)]
+        C, Cref, S = _run(dtype, tA, tB, alpha, opA, opB, beta, C0)
+        assert_within(C, Cref, S, f"{dtype} {pair} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_small_integers_bit_exact(dtype, pair):
+    tA, tB = pair
+    print(f"[lowp] small integers {dtype} {pair}", flush=True)
+    for (M, N, K) in [(300, 257, 513), (777, 555, 1001), (1024, 1024, 1024)]:
+        opA, opB, _ = _case(dtype, M, N, K, 7, dist="int")
+        C0 = synth.small_int(9, (M, N))
+        C, _, _ = _run(dtype, tA, tB, 3.0, opA, opB, -2.0, C0)
+        # Every partial sum is an integer far below 2^53, so float64 BLAS
+        # gives the exact product whatever its order.
+        want = 3 * (opA.astype(np.float64) @ opB.astype(np.float64)) - 2 * C0.astype(np.float64)
+        assert np.array_equal(C.astype(np.float64), want), (M, N, K)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_ragged_and_large_sampled(dtype, pair):
+    # The ragged shape (every edge partial, K tail) and 4096^3, checked on
+    # sampled elements including the last rows and columns.
+    tA, tB = pair
+    for (M, N, K) in [(3001, 2047, 4093), (4096, 4096, 4096)]:
+        print(f"[lowp] {M}x{N}x{K} {dtype} {pair}", flush=True)
+        opA, opB, C0 = _case(dtype, M, N, K, 31, dist="pm1" if M == 3001 else "u01")
+        A = synth.to_lowp_bits(_stored(opA, tA), dtype)
+        B = synth.to_lowp_bits(_stored(opB, tB), dtype)
+        C = gemm_lp(dtype, tA, tB, -0.5, A, B, 1.0, C0)
+        rng = np.random.default_rng(M)
+        rows = np.concatenate([rng.integers(0, M, 2000), np.arange(M - 40, M).repeat(10), rng.integers(0, M, 400)])
+        cols = np.concatenate([rng.integers(0, N, 2000), rng.integers(0, N, 400), np.arange(N - 40, N).repeat(10)])
+        want, S = oracle.gemm_ex_entries(tA, tB, -0.5, oracle.lowp_to_float32(A, dtype),
+                                         oracle.lowp_to_float32(B, dtype), 1.0, C0, rows, cols)
+        assert_within(C[rows, cols], want, S, f"{dtype} {pair} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_narrow_operands(dtype):
+    # Row-contiguous free extents 1..12: under 8 the one-per-element kernel,
+    # from 8 the matrix-core kernel with clamped, shifted edge reads.
+    print(f"[lowp] narrow {dtype}", flush=True)
+    for tA, tB in PAIRS:
+        for w in range(1, 13):
+            for (M, N) in [(w, 300), (300, w)]:
+                opA, opB, C0 = _case(dtype, M, N, 47, w)
+                C, Cref, S = _run(dtype, tA, tB, 1.25, opA, opB, 0.5, C0)
+                assert_within(C, Cref, S, f"{dtype} {(tA, tB)} {M}x{N}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_strided_views_and_misaligned_starts(dtype):
+    # Operands inside larger buffers (NaN encodings in the padding) at odd
+    # element offsets (2-byte aligned starts), C updated in place: every run
+    # equals the packed run bit for bit, and nothing outside C changes.
+    M, N, K = 150, 260, 333
+    for tA, tB in PAIRS:
+        print(f"[lowp] strided {dtype} {(tA, tB)}", flush=True)
+        opA, opB, C0 = _case(dtype, M, N, K, 500)
+        packed, Cref, S = _run(dtype, tA, tB, -0.75, opA, opB, 0.5, C0)
+        assert_within(packed, Cref, S, "packed")
+        for pads, offs in [((4, 4, 4), (0, 0, 0)), ((3, 5, 7), (0, 0, 0)), ((0, 0, 0), (1, 3, 5)),
+                           ((5, 1, 9), (3, 1, 2))]:
+            A = synth.to_lowp_bits(_stored(opA, tA), dtype)
+            B = synth.to_lowp_bits(_stored(opB, tB), dtype)
+            C, cbuf, ldc, off = gemm_lp(dtype, tA, tB, -0.75, A, B, 0.5, C0, ld_pad=pads, offset=offs,
+                                        return_buffer=True)
+            assert np.array_equal(C, packed), (tA, tB, pads, offs)
+            mask = np.ones(cbuf.shape, bool)
+            mask[(off + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]).ravel()] = False
+            assert (cbuf[mask] == SENTINEL).all()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_blas_read_rules_and_determinism(dtype):
+    print(f"[lowp] read rules {dtype}", flush=True)
+    M, N, K = 130, 140, 150
+    opA, opB, C0 = _case(dtype, M, N, K, 600)
+    # beta = 0: NaN in C is not read.
+    C, Cref, S = _run(dtype, False, False, 1.0, opA, opB, 0.0, np.full((M, N), np.nan, np.float32))
+    assert_within(C, oracle.gemm_ex(False, False, 1.0, opA, opB, 0.0, None)[0], S, "beta 0")
+    # alpha = 0: NaN encodings in A and B are not read.
+    nanA = np.full((M, K), 0x7FFF, np.uint16)
+    nanB = np.full((K, N), 0x7FFF, np.uint16)
+    C = gemm_lp(dtype, False, False, 0.0, nanA, nanB, -0.5, C0)
+    assert np.array_equal(C, np.float32(-0.5) * C0)
+    # Repeated runs are bit-identical.
+    first = _run(dtype, True, False, 1.0, opA, opB, 0.0, C0)[0]
+    for _ in range(3):
+        assert np.array_equal(_run(dtype, True, False, 1.0, opA, opB, 0.0, C0)[0], first)
+
+
+def test_lp_tensor_api():
+    print("[lowp] tensor API", flush=True)
+    M, N, K = 300, 200, 100
+    for dt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        X = synth.lowp_values(700, (K, M), dt)      # op(A) = X^T
+        Y = synth.lowp_values(701, (K, N), dt)
+        dX = torch.from_numpy(X).to(tdt).cuda()
+        dY = torch.from_numpy(Y).to(tdt).cuda()
+        C = sg.gemm(dX.t(), dY).cpu().numpy()
+        Cref, S = oracle.gemm_ex(True, False, 1.0, X, Y, 0.0, None)
+        assert_within(C, Cref, S, f"tensor API {dt}")
