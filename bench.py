@@ -18,6 +18,9 @@ Also reported:
   ladder        every kernel variant timed on the same workload;
   general_form  the best variant on the same sizes as C = alpha * op(A) *
                 op(B) + beta * C, for every transpose pair with beta 0 and 1;
+  lowp          the reduced-precision workload (bf16 and f16 operands, FP32
+                accumulation) on the same sizes, against the 16-bit matrix
+                peak, with sampled elements checked against the oracle;
   check         sampled elements compared with the oracle, and the
                 whole-matrix sum of C in double.
 """
@@ -40,6 +43,7 @@ if ROOT not in sys.path:
 # scalar-FMA rungs are rated against it too (they run measurably above half
 # of it, so half is not their ceiling).
 PEAK_FP32_TFLOPS = 157.3
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 / fp16 matrix peak (the reduced-precision workload)
 PEAK_HBM_GBS = 8000.0
 
 METRIC = "FP32 SGEMM TFLOP/s at 4096^3 on 1 MI355X; % of FP32 peak"
@@ -140,6 +144,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-ladder", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-general-form", action="store_true")
+    ap.add_argument("--no-lowp", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget of the CPU-baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -320,6 +325,43 @@ def main(argv=None) -> int:
                     log(f"general form {key}: {kms:.4f} ms, {general[key]['TFLOP/s']} TFLOP/s")
         out["general_form"] = general
         del dAt, dBt, dC2, plain
+
+    if not args.no_lowp:
+        import oracle
+        from oracle.check import excess
+        lowp = {}
+        rng = np.random.default_rng(2)
+        rows, cols = rng.integers(0, M, 256), rng.integers(0, N, 256)
+        for dt in ("bf16", "f16"):
+            Av = synth.lowp_values(synth.SEED_A, (M, K), dt)
+            Bv = synth.lowp_values(synth.SEED_B, (K, N), dt)
+            Ab, Bb = synth.to_lowp_bits(Av, dt), synth.to_lowp_bits(Bv, dt)
+            Bt = np.ascontiguousarray(Bb.T)
+            dAl = torch.from_numpy(Ab.view(np.int16)).to(dev)
+            for pair, Bst in (("nn", Bb), ("nt", Bt)):
+                dBl = torch.from_numpy(Bst.view(np.int16)).to(dev)
+                tb = 1 if pair == "nt" else 0
+
+                def call(dBl=dBl, tb=tb):
+                    rc = lib.sgemm_lp(sg.LP_TYPES[dt], 0, tb, M, N, K, 1.0, dAl.data_ptr(), K, dBl.data_ptr(),
+                                      K if tb else N, 0.0, dC.data_ptr(), N, stream.cuda_stream)
+                    if rc != 0:
+                        raise sg.SgemmError(rc)
+                tot, per_l = time_launches(call, 50, 10)
+                kms = sum(per_l) / len(per_l)
+                tf = f / (kms / 1e3) / 1e12
+                torch.cuda.synchronize()
+                Cl = dC.cpu().numpy()
+                ref, sabs = oracle.gemm_entries(oracle.lowp_to_float32(Ab, dt), oracle.lowp_to_float32(Bb, dt),
+                                                rows, cols)
+                worst = float(excess(Cl[rows, cols], ref, sabs).max())
+                lowp[f"{dt}_{pair}"] = {"kernel_ms_mean": round(kms, 5), "TFLOP/s": round(tf, 2),
+                                        "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                        "check_worst_error_over_bound": round(worst, 4)}
+                log(f"lowp {dt} {pair}: {kms:.4f} ms, {tf:.1f} TFLOP/s, check {worst:.3f}")
+                del dBl
+            del dAl
+        out["lowp"] = lowp
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the product")

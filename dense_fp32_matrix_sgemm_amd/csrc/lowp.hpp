@@ -451,10 +451,10 @@ hipError_t lp_launch_tiles(const LpProblem &p, hipStream_t stream)
 }
 
 #ifndef SGEMM_LP_BIG_TILE
-#define SGEMM_LP_BIG_TILE 256, 256, 32, 2, 2
+#define SGEMM_LP_BIG_TILE 256, 256, 32, 4, 2
 #endif
 #ifndef SGEMM_LP_MID_TILE
-#define SGEMM_LP_MID_TILE 128, 128, 32, 2, 2
+#define SGEMM_LP_MID_TILE 128, 128, 64, 4, 2
 #endif
 #ifndef SGEMM_LP_SMALL_TILE
 #define SGEMM_LP_SMALL_TILE 64, 64, 32, 2, 2
