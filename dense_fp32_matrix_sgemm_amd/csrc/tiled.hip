@@ -13,10 +13,10 @@
 // stored rows and written transposed into LDS.
 //
 // With T = 16 a wave64 covers four rows of the tile. The four rows read four
-// different words of As in the same instruction, so LDS rows are padded by one
+// different words of As in the same instruction, so As rows are padded by one
 // word to put them in different banks (the padding also spreads the
 // transposed writes); Bs is read as one contiguous row segment (a broadcast
-// across the four rows).
+// across the four rows) and is padded only when it is written transposed.
 #include "gemm.hpp"
 #include "tile_io.hpp"
 
@@ -28,8 +28,8 @@ constexpr int kT = 16;
 template <bool TA, bool TB>
 __global__ __launch_bounds__(kT *kT) void tiled_kernel(Problem p)
 {
-    __shared__ float As[kT][kT + 1];  // As[i][k] = op(A)[row0 + i][k0 + k]
-    __shared__ float Bs[kT][kT + 1];  // Bs[k][j] = op(B)[k0 + k][col0 + j]
+    __shared__ float As[kT][kT + 1];                 // As[i][k] = op(A)[row0 + i][k0 + k]
+    __shared__ float Bs[kT][kT + (TB ? 1 : 0)];      // Bs[k][j] = op(B)[k0 + k][col0 + j]
 
     const int tx = threadIdx.x, ty = threadIdx.y;
     const int col0 = blockIdx.x * kT;
