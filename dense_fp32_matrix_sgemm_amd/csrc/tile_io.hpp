@@ -138,50 +138,6 @@ __device__ __forceinline__ void update_n(float *base, std::int64_t ld, std::int6
         if (c + e < cols) p[e] = beta != 0.0f ? axpby(alpha, v[e], beta, p[e]) : alpha * v[e];
 }
 
-// Store N (1, 2 or 4) consecutive floats v[0..N-1] at (row, c ..) of C.
-// `inside` promises the whole run lies in C; with VEC it is then one store
-// of 4N bytes (alignment as for load4). Otherwise elements outside rows x
-// cols are dropped.
-template <bool VEC, int N>
-__device__ __forceinline__ void store_n(float *base, std::int64_t ld, std::int64_t row, int c, std::int64_t rows,
-                                        int cols, const float (&v)[N], bool inside)
-{
-    float *p = base + row * ld + c;
-    if (VEC && inside) {
-        if constexpr (N == 4) {
-            *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-        } else if constexpr (N == 2) {
-            *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
-        } else {
-            p[0] = v[0];
-        }
-        return;
-    }
-    if (row >= rows) return;
-#pragma unroll
-    for (int e = 0; e < N; ++e)
-        if (c + e < cols) p[e] = v[e];
-}
-
-// Store n (1..4) consecutive floats v[0..n-1] at (row, c ..) of C, dropping
-// elements outside rows x cols. With VEC and all four inside, one 16-byte
-// store (same alignment contract as load4).
-template <bool VEC>
-__device__ __forceinline__ void store4(float *base, std::int64_t ld, std::int64_t row, int c, std::int64_t rows,
-                                       int cols, float4 v)
-{
-    if (row >= rows) return;
-    float *p = base + row * ld + c;
-    if (VEC && c + 3 < cols) {
-        *reinterpret_cast<float4 *>(p) = v;
-        return;
-    }
-    if (c + 0 < cols) p[0] = v.x;
-    if (c + 1 < cols) p[1] = v.y;
-    if (c + 2 < cols) p[2] = v.z;
-    if (c + 3 < cols) p[3] = v.w;
-}
-
 // Work-group number -> output tile (tm, tn).
 //
 // The dispatcher hands consecutive work-group numbers to the eight XCDs in
