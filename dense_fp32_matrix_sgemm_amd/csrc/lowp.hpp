@@ -404,6 +404,316 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void lp
         lp_tile<Cfg, T, TA, TB, false>(p, tm, tn, lds);
 }
 
+// Direct-to-LDS pipeline for large products.
+//
+// The loop above moves every slab global -> registers -> LDS, and a slab's
+// loads have one slab of MFMAs to arrive. With 16-bit operands the matrix
+// cores finish a slab 8 times sooner, relative to the bytes it moves, than in
+// FP32, and that loop leaves them waiting on load latency and LDS bandwidth.
+// This one differs in three ways:
+//  * four waves (2 x 2) each multiply a 128 x 128 block of the 256 x 256
+//    tile (16 accumulator blocks, one wave per SIMD): per slab the waves read
+//    2/3 of the LDS bytes that eight 64 x 128 waves read;
+//  * chunks go straight from global memory into LDS (global_load_lds_dwordx4:
+//    one instruction writes 64 consecutive 16-byte chunks) through S stages:
+//    slab t + S - 1 is requested while slab t is multiplied, so a load has
+//    S - 2 slabs of MFMAs to arrive, with no staging registers and no LDS
+//    store instructions;
+//  * the DMA cannot pad rows, so instead the chunks of a stored row are
+//    permuted (an XOR swizzle chosen through which global chunk each lane
+//    fetches): KC rows of BK = 32 values hold chunk c at position
+//    c ^ g(r), g(r) = ((r >> 1) + (r >> 3)) & 3; FC rows of F values hold
+//    chunk j at position j ^ h(k), h(k) = ((k & 3) << 2) ^ (k & 2). With
+//    these the lanes of a ds_read_b128 or ds_read_b64_tr_b16 that the LDS
+//    serves together fall in distinct banks, for 32 four-byte banks serving
+//    128 bytes per cycle and for 64 serving 256.
+// A barrier per slab publishes the next stage (each wave first waits for its
+// own DMA of it, with the s_waitcnt count of the loads it may leave in
+// flight) and frees the stage the DMA issued after it overwrites. The
+// barrier is written out rather than taken from __syncthreads, whose fence
+// would wait for every load in flight, the later stages' included.
+//
+// Requirements (checked by the host): 16-byte aligned operands with leading
+// dimensions that are multiples of 8 elements, and an FC extent (N with B as
+// given, M with A transposed) that is a multiple of 8, so no chunk straddles
+// the edge. Edge tiles read clamped rows (KC) or the last chunk (FC) past the
+// edge; those values reach only rows and columns of C that are not stored. A
+// partial last slab of K is filled element by element with zeros past K.
+template <int F, int BK, bool KC_>
+struct LpDmaOperand {
+    static constexpr bool KC = KC_;
+    static constexpr int kRowChunks = KC ? BK / 8 : F / 8;  // chunks per stored row
+    static constexpr int kRowLen = KC ? BK : F;             // elements per stored row
+    static constexpr int kRows = KC ? F : BK;               // stored rows per slab
+    static constexpr int kElems = F * BK;                   // one stage
+    static constexpr int kInstrs = F * BK / 8 / 64;         // DMA instructions per slab
+    static_assert(BK == 32, "the KC swizzle is for rows of 4 chunks");
+    static_assert(KC || (F >= 128 && (F & (F - 1)) == 0), "the FC swizzle needs rows of 16 or more chunks");
+
+    __host__ __device__ static constexpr int swz(int row)
+    {
+        return KC ? (((row >> 1) + (row >> 3)) & 3) : (((row & 3) << 2) ^ (row & 2));
+    }
+    // Element offset, in one stage, of chunk c of stored row r.
+    __host__ __device__ static constexpr int lds_of(int r, int c) { return (r * kRowChunks + (c ^ swz(r))) * 8; }
+};
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_>
+struct LpDmaConfig : LpConfig<BM_, BN_, BK_, WAVES_M_, WAVES_N_> {
+    static constexpr int kStages = STAGES_;
+    static_assert(STAGES_ >= 3, "the DMA of slab t + S - 1 reuses the stage of slab t - 1");
+};
+
+// LDS byte address of a location in a __shared__ array.
+__device__ __forceinline__ unsigned lp_lds_address(const short *p)
+{
+    return static_cast<unsigned>(reinterpret_cast<std::uintptr_t>((const __attribute__((address_space(3))) short *)p));
+}
+
+// One global_load_lds_dwordx4: lane i copies the 16 bytes at its src to LDS
+// byte address lds + 16 i (lds is wave-uniform; the instruction takes it in
+// M0). Written as inline assembly so that the compiler does not see an LDS
+// store whose completion it would then wait for (with vmcnt(0)) before LDS
+// reads of other stages; the loop's own waits order it.
+__device__ __forceinline__ void lp_dma16(const std::uint16_t *src, unsigned lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                 "v"(src)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier; also a compiler barrier for
+// memory accesses.
+template <int N>
+__device__ __forceinline__ void lp_wait_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <class Cfg, LpType T, bool TA, bool TB>
+__device__ __forceinline__ void lp_dma_tile(const LpProblem &p, int tm, int tn, short *lds)
+{
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::kStages;
+    constexpr int NW = Cfg::WAVES_M * Cfg::WAVES_N;
+    using OpA = LpDmaOperand<BM, BK, !TA>;
+    using OpB = LpDmaOperand<BN, BK, TB>;
+    constexpr int NA = Cfg::WM / 32, NBl = Cfg::WN / 32;
+    constexpr int CA = OpA::kInstrs / NW, CB = OpB::kInstrs / NW;  // DMA instructions per wave per slab
+    constexpr int kStage = OpA::kElems + OpB::kElems;
+    constexpr int kPerSlab = CA + CB;
+    static_assert(CA * NW == OpA::kInstrs && CB * NW == OpB::kInstrs, "DMA must split evenly over the waves");
+    static_assert(BK == 32, "two steps of 16 k per slab");
+
+    const std::int64_t m0 = std::int64_t(tm) * BM;
+    const int n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
+    const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
+    const int n = p.K / BK;
+
+    lp_f32x16 acc[NA][NBl];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int b = 0; b < NBl; ++b) acc[a][b] = lp_f32x16{};
+
+    // Global element offset, from the slab's start, of the chunk this lane
+    // moves with DMA instruction q of an operand (instruction q * NW + wave
+    // of the slab; its lanes fill 64 consecutive chunk positions).
+    auto dma_offset = [&](auto op, int q, std::int64_t ld, std::int64_t f0, std::int64_t extent) -> std::int64_t {
+        using Op = decltype(op);
+        const int pos = (q * NW + wave) * 64 + lane;
+        const int r = pos / Op::kRowChunks;
+        const int c = (pos % Op::kRowChunks) ^ Op::swz(r);
+        if constexpr (Op::KC) {
+            std::int64_t f = f0 + r;
+            f = f < extent ? f : extent - 1;
+            return f * ld + 8 * c;
+        } else {
+            std::int64_t f = f0 + 8 * c;
+            f = f < extent ? f : extent - 8;
+            return std::int64_t(r) * ld + f;
+        }
+    };
+    const std::uint16_t *srca[CA];
+    const std::uint16_t *srcb[CB];
+#pragma unroll
+    for (int q = 0; q < CA; ++q) srca[q] = p.A + dma_offset(OpA{}, q, p.lda, m0, p.M);
+#pragma unroll
+    for (int q = 0; q < CB; ++q) srcb[q] = p.B + dma_offset(OpB{}, q, p.ldb, n0, p.N);
+    const std::int64_t slab_a = OpA::KC ? BK : BK * p.lda, slab_b = OpB::KC ? BK : BK * p.ldb;
+
+    auto stage_a = [&](int st) { return lds + st * kStage; };
+    auto stage_b = [&](int st) { return lds + st * kStage + OpA::kElems; };
+    // DMA instruction i (0 .. kPerSlab - 1) of slab `slab` into stage st:
+    // the A instructions first, then the B ones.
+    const unsigned lds_bytes = lp_lds_address(lds);
+    auto dma_one = [&](int i, int slab, int st) {
+        if (i < CA)
+            lp_dma16(srca[i] + slab * slab_a, lds_bytes + 2u * unsigned(st * kStage + (i * NW + wave) * 512));
+        else
+            lp_dma16(srcb[i - CA] + slab * slab_b,
+                     lds_bytes + 2u * unsigned(st * kStage + OpA::kElems + ((i - CA) * NW + wave) * 512));
+    };
+
+    // Per-lane fragment offsets within a stage, for step s of block b.
+    const int l32 = lane % 32, h = lane / 32;
+    auto frag_offsets = [&](auto op, int w0, int (&off)[2][4]) {
+        using Op = decltype(op);
+        if constexpr (Op::KC) {
+            // Row w0 + 32 b + l32, chunk 2 s + h.
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) off[s][b] = Op::lds_of(w0 + 32 * b + l32, 2 * s + h);
+        } else {
+            // Lane 4 r + q of 16-lane group g: row 16 s + 8 (g / 2) + r,
+            // elements w0 + 32 b + 16 (g % 2) + 4 q .. + 3.
+            const int g = lane / 16, i = lane % 16, r = i / 4, q = i % 4;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int k = 16 * s + 8 * (g / 2) + r;
+                    const int f = w0 + 32 * b + 16 * (g % 2) + 4 * q;
+                    off[s][b] = Op::lds_of(k, f / 8) + f % 8;
+                }
+        }
+    };
+    static_assert(NA == 4 && NBl == 4, "offset tables hold four blocks");
+    int offa[2][4], offb[2][4];
+    frag_offsets(OpA{}, wm0, offa);
+    frag_offsets(OpB{}, wn0, offb);
+
+    auto read_op = [&](auto op, lp_i16x8 &v, const short *stage, int o) {
+        using Op = decltype(op);
+        if constexpr (Op::KC) {
+            v = *reinterpret_cast<const lp_i16x8 *>(stage + o);
+        } else {
+            const lp_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp_lds_i16x4 *)(stage + o));
+            const lp_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp_lds_i16x4 *)(stage + o + 4 * Op::kRowLen));
+            v = lp_i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    };
+    // Fragments of step s, block u (A blocks, then B blocks), into slot `slot`.
+    lp_i16x8 fa[2][NA], fb[2][NBl];
+    constexpr int NU = NA + NBl;
+    auto read_unit = [&](int u, int st, int s, int slot) {
+        if (u < NA)
+            read_op(OpA{}, fa[slot][u], stage_a(st), offa[s][u]);
+        else
+            read_op(OpB{}, fb[slot][u - NA], stage_b(st), offb[s][u - NA]);
+    };
+    auto mfma_one = [&](int slot, int i) {
+        const int a = i / NBl, b = i % NBl;
+        acc[a][b] = mma16<T>(fa[slot][a], fb[slot][b], acc[a][b]);
+    };
+
+    // One step's MFMAs with the fragment reads for the other slot spread one
+    // after each of the first MFMAs (so reads neither hold back an MFMA nor
+    // wait until the MFMAs that need them), and, after the barrier, the
+    // slab's DMA instructions spread the same way (each is its own
+    // scheduling region, which keeps the order as written).
+    constexpr int kReads = (OpA::KC ? NA : 2 * NA) + (OpB::KC ? NBl : 2 * NBl);
+    constexpr int kMfmas = NA * NBl;
+    static_assert(kReads <= kMfmas && NU <= kMfmas && kPerSlab <= kMfmas, "one read and one DMA per MFMA at most");
+    auto step = [&](int slot, int rd_st, int rd_s, bool reads, int dma_slab, bool dmas) {
+        const int dma_st = (rd_st + S - 2) % S;  // with dmas: the stage of slab t - 1
+#pragma unroll
+        for (int i = 0; i < kMfmas; ++i) {
+            if (dmas && i < kPerSlab) dma_one(i, dma_slab, dma_st);
+            mfma_one(slot, i);
+            if (reads && i < NU) read_unit(i, rd_st, rd_s, slot ^ 1);
+        }
+#pragma unroll
+        for (int i = 0; i < kMfmas; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kLpSchedMfma, 1, 0);
+            if (reads && i < kReads) __builtin_amdgcn_sched_group_barrier(kLpSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if (n > 0) {
+        // Slab indices past the last are clamped to it: the loop then issues
+        // the same DMA every iteration (the repeats land in the stage that is
+        // free anyway), waits with one count, and has no branches, which
+        // keeps the 256 accumulator registers where they are.
+        auto last = [&](int slab) { return slab < n ? slab : n - 1; };
+#pragma unroll
+        for (int i = 0; i < S - 1; ++i)
+#pragma unroll
+            for (int d = 0; d < kPerSlab; ++d) dma_one(d, last(i), i);
+        lp_wait_barrier<(S - 2) * kPerSlab>();
+#pragma unroll
+        for (int u = 0; u < NU; ++u) read_unit(u, 0, 0, 0);
+        // Step 0 of slab t multiplies while step 1's fragments load; slab
+        // t + 1 is published (slabs t + 2 .. t + S - 2 may still be in
+        // flight); step 1 multiplies while slab t + S - 1 is requested into
+        // the stage slab t - 1 used and slab t + 1's first fragments load (in
+        // the last iteration, from a stage nobody uses again).
+        for (int t = 0; t < n; ++t) {
+            step(0, t % S, 1, true, 0, false);
+            lp_wait_barrier<(S - 3) * kPerSlab>();
+            step(1, (t + 1) % S, 0, true, last(t + S - 1), true);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated DMAs
+    }
+    if (n * BK < p.K) {
+        // Partial last slab into stage 0: k >= K reads as zero, free indices
+        // past the operand's extent are clamped into it.
+        lp_wait_barrier<0>();
+        const int k0 = n * BK;
+        auto partial = [&](auto op, const std::uint16_t *X, std::int64_t ld, std::int64_t f0, std::int64_t extent,
+                           short *dst) {
+            using Op = decltype(op);
+#pragma unroll 1
+            for (int e = tid; e < Op::kRows * Op::kRowLen; e += Cfg::kThreads) {
+                const int r = e / Op::kRowLen, c = e % Op::kRowLen;
+                const int k = Op::KC ? c : r;
+                const std::int64_t f = f0 + (Op::KC ? r : c);
+                const std::int64_t fc = f < extent ? f : extent - 1;
+                const std::int64_t at = Op::KC ? fc * ld + k0 + k : std::int64_t(k0 + k) * ld + fc;
+                dst[Op::lds_of(r, c / 8) + c % 8] = k0 + k < p.K ? short(X[at]) : short(0);
+            }
+        };
+        partial(OpA{}, p.A, p.lda, m0, p.M, stage_a(0));
+        partial(OpB{}, p.B, p.ldb, n0, p.N, stage_b(0));
+        lp_wait_barrier<0>();
+#pragma unroll
+        for (int u = 0; u < NU; ++u) read_unit(u, 0, 0, 0);
+        step(0, 0, 1, true, 0, false);
+        step(1, 0, 0, false, 0, false);
+    }
+
+    // Epilogue: register r of block (a, b) is row 32a + 8(r/4) + 4h + r%4 and
+    // column 32b + l % 32 of the wave tile.
+    const bool inside = m0 + BM <= p.M && n0 + BN <= p.N;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const std::int64_t row = m0 + wm0 + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
+#pragma unroll
+            for (int b = 0; b < NBl; ++b) {
+                const float v[1] = {acc[a][b][r]};
+                update_n<1>(p.C, p.ldc, row, n0 + wn0 + 32 * b + l32, p.M, p.N, v, inside, p.alpha, p.beta);
+            }
+        }
+}
+
+template <class Cfg, LpType T, bool TA, bool TB>
+__global__ __launch_bounds__(Cfg::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void lp_dma_kernel(
+    LpProblem p, int tiles_m)
+{
+    __shared__ __attribute__((aligned(16))) short lds[Cfg::kStages * (Cfg::BM + Cfg::BN) * Cfg::BK];
+    int tm, tn;
+    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, Cfg::kGroupM, tm, tn);
+    lp_dma_tile<Cfg, T, TA, TB>(p, tm, tn, lds);
+}
+
 // Products whose FC operand is under 8 wide: one work-item per element of C,
 // products of the widened values summed with FP32 fused multiply-adds.
 template <LpType T, bool TA, bool TB>
@@ -424,14 +734,18 @@ __global__ __launch_bounds__(256) void lp_naive_kernel(LpProblem p)
 
 // Tile grids beyond 2^22 tiles run as bands (row bands of op(A) and C,
 // column bands of op(B) and C), as the FP32 launches do.
-template <class Cfg, LpType T, bool TA, bool TB>
+template <class Cfg, LpType T, bool TA, bool TB, bool DMA = false>
 hipError_t lp_launch_tiles(const LpProblem &p, hipStream_t stream)
 {
     constexpr std::int64_t kMaxTiles = std::int64_t(1) << 22;
     const std::int64_t tiles_n_all = (std::int64_t(p.N) + Cfg::BN - 1) / Cfg::BN;
     const std::int64_t band_tn = tiles_n_all < kMaxTiles ? tiles_n_all : kMaxTiles;
     const std::int64_t band_tm = kMaxTiles / band_tn;
-    const void *kernel = reinterpret_cast<const void *>(&lp_tiles_kernel<Cfg, T, TA, TB>);
+    const void *kernel;
+    if constexpr (DMA)
+        kernel = reinterpret_cast<const void *>(&lp_dma_kernel<Cfg, T, TA, TB>);
+    else
+        kernel = reinterpret_cast<const void *>(&lp_tiles_kernel<Cfg, T, TA, TB>);
     for (std::int64_t r0 = 0; r0 < p.M; r0 += band_tm * Cfg::BM) {
         for (std::int64_t c0 = 0; c0 < p.N; c0 += band_tn * Cfg::BN) {
             LpProblem q = p;
@@ -459,6 +773,10 @@ hipError_t lp_launch_tiles(const LpProblem &p, hipStream_t stream)
 #ifndef SGEMM_LP_SMALL_TILE
 #define SGEMM_LP_SMALL_TILE 64, 64, 32, 2, 2
 #endif
+#ifndef SGEMM_LP_DMA_TILE
+#define SGEMM_LP_DMA_TILE 256, 256, 32, 2, 2, 4
+#endif
+using LpDmaCfg = LpDmaConfig<SGEMM_LP_DMA_TILE>;
 using LpBigCfg = LpConfig<SGEMM_LP_BIG_TILE>;
 using LpMidCfg = LpConfig<SGEMM_LP_MID_TILE>;
 using LpSmallCfg = LpConfig<SGEMM_LP_SMALL_TILE>;
@@ -467,6 +785,20 @@ template <class Cfg>
 std::int64_t lp_tiles(const LpProblem &p)
 {
     return ((std::int64_t(p.M) + Cfg::BM - 1) / Cfg::BM) * ((std::int64_t(p.N) + Cfg::BN - 1) / Cfg::BN);
+}
+
+// Whether the direct-to-LDS kernel can take a product: 16-byte aligned
+// operands and rows, and an FC extent that is a multiple of 8.
+template <bool TA, bool TB>
+bool lp_dma_ok(const LpProblem &p)
+{
+#if defined(SGEMM_LP_NO_DMA)
+    return false;
+#else
+    const auto aligned = [](const void *x) { return (reinterpret_cast<std::uintptr_t>(x) & 15) == 0; };
+    return aligned(p.A) && aligned(p.B) && p.lda % 8 == 0 && p.ldb % 8 == 0 && (!TA || p.M % 8 == 0) &&
+           (TB || p.N % 8 == 0);
+#endif
 }
 
 // The largest tile shape whose tiles give every compute unit at least one.
@@ -482,6 +814,7 @@ hipError_t lp_launch(const LpProblem &p, hipStream_t stream)
                                0, stream);
     }
     const std::int64_t fill = p.cus > 0 ? p.cus : 256;
+    if (lp_tiles<LpDmaCfg>(p) >= fill && lp_dma_ok<TA, TB>(p)) return lp_launch_tiles<LpDmaCfg, T, TA, TB, true>(p, stream);
     if (lp_tiles<LpBigCfg>(p) >= fill) return lp_launch_tiles<LpBigCfg, T, TA, TB>(p, stream);
     if (lp_tiles<LpMidCfg>(p) >= fill) return lp_launch_tiles<LpMidCfg, T, TA, TB>(p, stream);
     return lp_launch_tiles<LpSmallCfg, T, TA, TB>(p, stream);

@@ -106,6 +106,67 @@ def test_lp_ragged_and_large_sampled(dtype, pair):
         assert_within(C[rows, cols], want, S, f"{dtype} {pair} {M}x{N}x{K}")
 
 
+def _sampled(dtype, tA, tB, M, N, K, seed, alpha=-0.5, beta=1.0, **kw):
+    """Run one product and check ~5000 sampled elements (with the last rows
+    and columns, and the whole bottom-right 256 x 256 tile) with the oracle."""
+    opA, opB, C0 = _case(dtype, M, N, K, seed)
+    A = synth.to_lowp_bits(_stored(opA, tA), dtype)
+    B = synth.to_lowp_bits(_stored(opB, tB), dtype)
+    C = gemm_lp(dtype, tA, tB, alpha, A, B, beta, C0, **kw)
+    rng = np.random.default_rng(seed)
+    r0, c0 = (M - 1) // 256 * 256, (N - 1) // 256 * 256
+    rr, cc = np.meshgrid(np.arange(r0, M), np.arange(c0, N), indexing="ij")
+    rows = np.concatenate([rng.integers(0, M, 2000), np.arange(M - 40, M).repeat(10), rng.integers(0, M, 400),
+                           rr.ravel()])
+    cols = np.concatenate([rng.integers(0, N, 2000), rng.integers(0, N, 400), np.arange(N - 40, N).repeat(10),
+                           cc.ravel()])
+    want, S = oracle.gemm_ex_entries(tA, tB, alpha, oracle.lowp_to_float32(A, dtype), oracle.lowp_to_float32(B, dtype),
+                                     beta, C0, rows, cols)
+    assert_within(C[rows, cols], want, S, f"{dtype} {(tA, tB)} {M}x{N}x{K} {kw}")
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_direct_to_lds_edges(dtype, pair):
+    # Products large enough for the direct-to-LDS 256 x 256 kernel (at least
+    # one tile per compute unit) with partial tiles on both edges (the free
+    # index that is contiguous in memory a multiple of 8, as that kernel
+    # needs) and a partial last slab of K.
+    tA, tB = pair
+    print(f"[lowp] direct-to-LDS edges {dtype} {pair}", flush=True)
+    _sampled(dtype, tA, tB, 4000, 4104, 1000, 61)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_direct_to_lds_fallbacks(dtype):
+    # The same tile count with one condition of the direct-to-LDS kernel
+    # broken each time, so the register-staged kernel takes the product: an
+    # FC extent that is not a multiple of 8, a leading dimension that is not,
+    # and an operand start that is not 16-byte aligned.
+    print(f"[lowp] direct-to-LDS fallbacks {dtype}", flush=True)
+    _sampled(dtype, True, False, 4004, 4104, 520, 71)           # M % 8 with A transposed
+    _sampled(dtype, False, False, 4096, 4100, 520, 72)          # N % 8 with B as given
+    _sampled(dtype, False, True, 4096, 4096, 520, 73, ld_pad=(4, 0, 0))
+    _sampled(dtype, False, False, 4096, 4096, 520, 74, offset=(0, 3, 0))
+
+
+@pytest.mark.parametrize("pair", [(False, False), (True, True)], ids=["nn", "tt"])
+def test_lp_direct_to_lds_small_integers_bit_exact(pair):
+    # Small integers: every partial sum is an integer below 2^24, so the
+    # result is exact whatever the summation order; checked against float64
+    # matrix products.
+    tA, tB = pair
+    M, N, K = 4096, 4096, 1024
+    print(f"[lowp] direct-to-LDS small integers {pair}", flush=True)
+    opA = synth.lowp_values(81, (M, K), "bf16", "int")
+    opB = synth.lowp_values(82, (K, N), "bf16", "int")
+    A = synth.to_lowp_bits(_stored(opA, tA), "bf16")
+    B = synth.to_lowp_bits(_stored(opB, tB), "bf16")
+    C = gemm_lp("bf16", tA, tB, 1.0, A, B, 0.0, np.zeros((M, N), np.float32))
+    want = opA.astype(np.float64) @ opB.astype(np.float64)
+    assert np.array_equal(C.astype(np.float64), want)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_lp_narrow_operands(dtype):
     # Row-contiguous free extents 1..12: under 8 the one-per-element kernel,
