@@ -34,6 +34,12 @@
 // last slab of K is loaded element by element with zeros past K. This needs
 // the FC operand at least 8 wide; narrower products take a one-thread-per-
 // element kernel.
+//
+// Products large enough for one 256 x 256 tile per compute unit, with
+// 16-byte aligned rows, take a second kernel (lp_dma_tile below): four waves
+// of 128 x 128, operands moved global -> LDS by DMA through four swizzled
+// stages. Both kernels read the same k order per lane, so a product gives the
+// same terms in the same order whichever of them runs.
 #pragma once
 
 #include <type_traits>

@@ -150,6 +150,23 @@ def test_lp_direct_to_lds_fallbacks(dtype):
     _sampled(dtype, False, False, 4096, 4096, 520, 74, offset=(0, 3, 0))
 
 
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_lp_direct_to_lds_matches_register_path_bitwise(pair):
+    # Both kernels feed each lane the same k of every step of 16 and walk the
+    # steps in the same order, so the same product gives the same bits
+    # whichever runs: here the direct-to-LDS kernel (aligned A) against the
+    # register-staged one (A starting one element into its buffer).
+    tA, tB = pair
+    M, N, K = 4096, 4096, 520
+    print(f"[lowp] direct-to-LDS vs register path {pair}", flush=True)
+    opA, opB, C0 = _case("bf16", M, N, K, 91)
+    A = synth.to_lowp_bits(_stored(opA, tA), "bf16")
+    B = synth.to_lowp_bits(_stored(opB, tB), "bf16")
+    C1 = gemm_lp("bf16", tA, tB, 0.75, A, B, -1.0, C0)
+    C2 = gemm_lp("bf16", tA, tB, 0.75, A, B, -1.0, C0, offset=(1, 0, 0))
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
+
+
 @pytest.mark.parametrize("pair", [(False, False), (True, True)], ids=["nn", "tt"])
 def test_lp_direct_to_lds_small_integers_bit_exact(pair):
     # Small integers: every partial sum is an integer below 2^24, so the
