@@ -23,6 +23,12 @@ Also reported:
                 peak, with sampled elements checked against the oracle;
   check         sampled elements compared with the oracle, and the
                 whole-matrix sum of C in double.
+
+With --all-configs it instead times every kernel variant on every workload of
+the method's configuration table (128^3, 1024^3, 2048^3, 4096^3 and the ragged
+3001 x 2047 x 4093 on U[-1, 1)): median and minimum launch time, each result
+checked on sampled elements, the CPU oracle timed on each whole product (and on
+one thread at 128^3 and 1024^3), and the shader clock read before and after.
 """
 
 from __future__ import annotations
@@ -132,6 +138,99 @@ def cpu_baseline(A, B, target_s: float):
     }
 
 
+# The method's configuration table: (M, N, K, value distribution).
+CONFIGS = [(128, 128, 128, "u01"), (1024, 1024, 1024, "u01"), (2048, 2048, 2048, "u01"),
+           (4096, 4096, 4096, "u01"), (3001, 2047, 4093, "pm1")]
+
+
+def read_sclk():
+    """Current shader clock level of each GPU as the driver reports it (the
+    starred line of pp_dpm_sclk), or None where the file is not readable."""
+    import glob
+    out = {}
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                cur = [line.strip() for line in f if line.strip().endswith("*")]
+        except OSError:
+            continue
+        out[path.split("/")[4]] = cur[0] if cur else None
+    return out or None
+
+
+def oracle_seconds_one_thread(M: int, N: int, K: int, dist: str) -> float:
+    """The oracle on one host thread, in a child process (its OpenMP thread
+    count is fixed at start-up)."""
+    import subprocess
+    code = ("import sys, time, synth, oracle\n"
+            f"A, B = synth.operands({M}, {N}, {K}, '{dist}')\n"
+            "t0 = time.perf_counter(); oracle.gemm(A, B); print(time.perf_counter() - t0)\n")
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600, check=True)
+    return float(r.stdout.strip().splitlines()[-1])
+
+
+def all_configs(lib, sg, dev) -> dict:
+    """Every variant on every configuration: timing, sampled check, oracle."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    from oracle.check import excess
+    stream = torch.cuda.current_stream()
+    result = {"sclk_before": read_sclk(), "oracle_threads": oracle.num_threads(), "configs": []}
+    for (M, N, K, dist) in CONFIGS:
+        log(f"all-configs: {M}x{N}x{K} ({dist})")
+        A, B = synth.operands(M, N, K, dist)
+        dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        dC = torch.zeros((M, N), dtype=torch.float32, device=dev)
+        f = flops(M, N, K)
+        rng = np.random.default_rng(M + N + K)
+        rows = np.concatenate([[0, M - 1], rng.integers(0, M, 1022)])
+        cols = np.concatenate([[N - 1, 0], rng.integers(0, N, 1022)])
+        ref, sabs = oracle.gemm_entries(A, B, rows, cols)
+        entry = {"M": M, "N": N, "K": K, "values": dist, "variants": {}}
+        for name in ("naive", "tiled", "regblock", "mfma"):
+            code = sg.VARIANTS[name]
+
+            def call(code=code):
+                rc = lib.sgemm(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N,
+                               stream.cuda_stream, code)
+                if rc != 0:
+                    raise sg.SgemmError(rc)
+            dC.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+            worst = float(excess(dC.cpu().numpy()[rows, cols], ref, sabs).max())
+            t0 = time.perf_counter()
+            call()
+            torch.cuda.synchronize()
+            one = time.perf_counter() - t0
+            reps = int(max(50, min(2000, 0.1 / max(one, 1e-6))))
+            _, per = time_launches(call, reps, 3)
+            med, mn = float(np.median(per)), min(per)
+            entry["variants"][name] = {
+                "reps": reps, "ms_median": round(med, 5), "ms_min": round(mn, 5),
+                "TFLOP/s_median": round(f / (med / 1e3) / 1e12, 3), "TFLOP/s_max": round(f / (mn / 1e3) / 1e12, 3),
+                "frac_of_fp32_peak_median": round(f / (med / 1e3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                "check_worst_error_over_bound": round(worst, 4)}
+            log(f"  {name}: median {med:.4f} ms, min {mn:.4f} ms, "
+                f"{entry['variants'][name]['TFLOP/s_median']} TFLOP/s, check {worst:.3f}")
+        t0 = time.perf_counter()
+        oracle.gemm(A, B)
+        dt = time.perf_counter() - t0
+        entry["oracle"] = {"seconds": round(dt, 4), "TFLOP/s": round(f / dt / 1e12, 6)}
+        if M in (128, 1024) and M == N == K:
+            dt1 = oracle_seconds_one_thread(M, N, K, dist)
+            entry["oracle_one_thread"] = {"seconds": round(dt1, 4), "TFLOP/s": round(f / dt1 / 1e12, 6)}
+        result["configs"].append(entry)
+        del dA, dB, dC
+    result["sclk_after"] = read_sclk()
+    return result
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +246,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-lowp", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget of the CPU-baseline sample")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the headline, time every variant on every configuration "
+                         "and the CPU oracle on each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the product, time a plain 256 MiB device copy "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -183,6 +285,10 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
                           "ms_per_copy": round(ms, 5),
                           "GB_per_s": round(8 * n / (ms / 1e3) / 1e9, 1)}))
+        return 0
+
+    if args.all_configs:
+        print(json.dumps({"metric": METRIC, "all_configs": all_configs(lib, sg, dev)}), flush=True)
         return 0
 
     M = N = K = args.size
