@@ -27,8 +27,10 @@ Also reported:
 With --all-configs it instead times every kernel variant on every workload of
 the method's configuration table (128^3, 1024^3, 2048^3, 4096^3 and the ragged
 3001 x 2047 x 4093 on U[-1, 1)): median and minimum launch time, each result
-checked on sampled elements, the CPU oracle timed on each whole product (and on
-one thread at 128^3 and 1024^3), and the shader clock read before and after.
+checked on sampled elements (and the matrix-core variant through sgemm_ex_ws
+where the library would split the product), the CPU oracle timed on each whole
+product (and on one thread at 128^3 and 1024^3), and the shader clock read
+before and after.
 """
 
 from __future__ import annotations
@@ -218,6 +220,32 @@ def all_configs(lib, sg, dev) -> dict:
                 "check_worst_error_over_bound": round(worst, 4)}
             log(f"  {name}: median {med:.4f} ms, min {mn:.4f} ms, "
                 f"{entry['variants'][name]['TFLOP/s_median']} TFLOP/s, check {worst:.3f}")
+        # The matrix-core variant through sgemm_ex_ws, where the library puts
+        # the product on its split schedule.
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        need = sg.sgemm_ex_workspace_size(sg.SGEMM_OP_N, sg.SGEMM_OP_N, M, N, K, cus)
+        if need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+            def call_ws():
+                rc = lib.sgemm_ex_ws(0, 0, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, dC.data_ptr(), N,
+                                     ws.data_ptr(), need, stream.cuda_stream, sg.SGEMM_MFMA)
+                if rc != 0:
+                    raise sg.SgemmError(rc)
+            dC.fill_(float("nan"))
+            call_ws()
+            torch.cuda.synchronize()
+            worst = float(excess(dC.cpu().numpy()[rows, cols], ref, sabs).max())
+            _, per = time_launches(call_ws, 100, 3)
+            med, mn = float(np.median(per)), min(per)
+            entry["variants"]["mfma_split"] = {
+                "reps": 100, "workspace_bytes": need, "ms_median": round(med, 5), "ms_min": round(mn, 5),
+                "TFLOP/s_median": round(f / (med / 1e3) / 1e12, 3), "TFLOP/s_max": round(f / (mn / 1e3) / 1e12, 3),
+                "frac_of_fp32_peak_median": round(f / (med / 1e3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                "check_worst_error_over_bound": round(worst, 4)}
+            log(f"  mfma_split: median {med:.4f} ms, {entry['variants']['mfma_split']['TFLOP/s_median']} TFLOP/s, "
+                f"check {worst:.3f}")
+            del ws
         t0 = time.perf_counter()
         oracle.gemm(A, B)
         dt = time.perf_counter() - t0

@@ -69,8 +69,9 @@ VARIANTS = {"best": SGEMM_BEST, "naive": SGEMM_NAIVE, "tiled": SGEMM_TILED,
             "regblock": SGEMM_REGBLOCK, "mfma": SGEMM_MFMA}
 
 # Symbols the shared library exports (the functions of include/sgemm.h).
-EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args", "sgemm_lp", "sgemm_lp_check_args",
-           "sgemm_status_string", "sgemm_variant_name", "sgemm_best_variant", "sgemm_mfma_tile")
+EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args", "sgemm_ex_ws", "sgemm_ex_ws_check_args",
+           "sgemm_ex_workspace_size", "sgemm_lp", "sgemm_lp_check_args", "sgemm_status_string", "sgemm_variant_name",
+           "sgemm_best_variant", "sgemm_mfma_tile")
 
 _lib = None
 
@@ -104,6 +105,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_ex.restype = i
     lib.sgemm_ex_check_args.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, i]
     lib.sgemm_ex_check_args.restype = i
+    sz = ctypes.c_size_t
+    lib.sgemm_ex_ws.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp, sz, vp, i]
+    lib.sgemm_ex_ws.restype = i
+    lib.sgemm_ex_ws_check_args.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp, sz, i]
+    lib.sgemm_ex_ws_check_args.restype = i
+    lib.sgemm_ex_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.sgemm_ex_workspace_size.restype = sz
     lib.sgemm_lp.argtypes = [i, i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp]
     lib.sgemm_lp.restype = i
     lib.sgemm_lp_check_args.argtypes = [i, i, i, i, i, i, f, vp, i, vp, i, f, vp, i]
@@ -133,6 +141,23 @@ def sgemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, variant) -> int:
 def sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant) -> int:
     return load_library().sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                    stream, variant)
+
+
+def sgemm_ex_ws(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, stream,
+                variant) -> int:
+    return load_library().sgemm_ex_ws(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                                      workspace_bytes, stream, variant)
+
+
+def sgemm_ex_ws_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes,
+                           variant) -> int:
+    return load_library().sgemm_ex_ws_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                                 workspace, workspace_bytes, variant)
+
+
+def sgemm_ex_workspace_size(transA: int, transB: int, M: int, N: int, K: int, cus: int = 0) -> int:
+    """Workspace bytes sgemm_ex_ws needs for this product (0: it would not split it)."""
+    return int(load_library().sgemm_ex_workspace_size(transA, transB, M, N, K, cus))
 
 
 def sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant) -> int:
@@ -206,7 +231,7 @@ def _check_tensor(t, name):
         raise ValueError(f"{name} must be on a GPU device")
 
 
-def gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best"):
+def gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best", workspace=None):
     """C = alpha * A @ B + beta * C for float32 GPU tensors A (M x K), B (K x N).
 
     A and B may be row-major or column-major views (a transposed view such
@@ -214,6 +239,9 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best"):
     copy). C (M x N, row-major, rows possibly padded) is updated in place; it
     is read only when beta != 0, and allocated when None (then beta must be
     0). The kernels are enqueued on the current stream of A's device.
+    ``workspace``, a contiguous GPU tensor on A's device, lets the library use
+    the split schedule (sgemm_ex_ws) where it is faster; its size in bytes
+    should be at least sgemm_ex_workspace_size() for the product.
     """
     import torch
 
@@ -243,9 +271,17 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best"):
         raise ValueError("C must be row-major (unit column stride)")
     with torch.cuda.device(A.device):
         stream = torch.cuda.current_stream(A.device).cuda_stream
-        rc = sgemm_ex(ta, tb, M, N, K, float(alpha), A.data_ptr() or None, lda,
-                      B.data_ptr() or None, ldb, float(beta), C.data_ptr() or None, ldc,
-                      stream or None, _variant_code(variant))
+        if workspace is None:
+            rc = sgemm_ex(ta, tb, M, N, K, float(alpha), A.data_ptr() or None, lda,
+                          B.data_ptr() or None, ldb, float(beta), C.data_ptr() or None, ldc,
+                          stream or None, _variant_code(variant))
+        else:
+            if not isinstance(workspace, torch.Tensor) or workspace.device != A.device or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous tensor on A's device")
+            rc = sgemm_ex_ws(ta, tb, M, N, K, float(alpha), A.data_ptr() or None, lda,
+                             B.data_ptr() or None, ldb, float(beta), C.data_ptr() or None, ldc,
+                             workspace.data_ptr() or None, workspace.numel() * workspace.element_size(),
+                             stream or None, _variant_code(variant))
     if rc != SGEMM_OK:
         raise SgemmError(rc)
     return C

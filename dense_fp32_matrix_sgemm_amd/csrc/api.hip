@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstddef>
 #include <cstring>
 
 #include "gemm.hpp"
@@ -41,7 +42,39 @@ hipError_t launch_mfma(const sgemm_impl::Problem &p, hipStream_t s)
     return p.tb ? sgemm_impl::launch_mfma_nt(p, s) : sgemm_impl::launch_mfma_nn(p, s);
 }
 
+hipError_t launch_mfma_sk(const sgemm_impl::Problem &p, sgemm_impl::MfmaTile tile, float *ws, int grid, hipStream_t s)
+{
+    if (p.ta)
+        return p.tb ? sgemm_impl::launch_mfma_sk_tt(p, tile, ws, grid, s) : sgemm_impl::launch_mfma_sk_tn(p, tile, ws, grid, s);
+    return p.tb ? sgemm_impl::launch_mfma_sk_nt(p, tile, ws, grid, s) : sgemm_impl::launch_mfma_sk_nn(p, tile, ws, grid, s);
+}
+
 }  // namespace
+
+extern "C" int sgemm_ex_ws(int transA, int transB, int M, int N, int K, float alpha, const float *A, int lda,
+                           const float *B, int ldb, float beta, float *C, int ldc, void *workspace,
+                           std::size_t workspace_bytes, void *stream, int variant)
+{
+    const int rc = sgemm_ex_ws_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                                          workspace_bytes, variant);
+    if (rc != SGEMM_OK) return rc;
+    const bool product = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
+    const int v = variant == SGEMM_BEST ? sgemm_best_variant(M, N, K) : variant;
+    if (product && v == SGEMM_MFMA && workspace != nullptr && workspace_bytes > 0) {
+        const int cus = current_gfx950_cus();
+        if (cus == 0) return SGEMM_ERR_DEVICE;
+        const std::size_t need = sgemm_ex_workspace_size(transA, transB, M, N, K, cus);
+        if (need > 0 && need <= workspace_bytes) {
+            const sgemm_impl::SplitChoice c = sgemm_impl::choose_split(M, N, K, cus);
+            const sgemm_impl::Problem p{A,     B,    C,   lda, ldb, ldc, M, N, K, cus, transA == SGEMM_OP_T,
+                                        transB == SGEMM_OP_T, alpha, beta, c.tile};
+            const hipError_t err =
+                launch_mfma_sk(p, c.tile, static_cast<float *>(workspace), c.grid, static_cast<hipStream_t>(stream));
+            return err == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+        }
+    }
+    return sgemm_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+}
 
 extern "C" int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha, const float *A, int lda,
                         const float *B, int ldb, float beta, float *C, int ldc, void *stream, int variant)

@@ -59,6 +59,24 @@ extern "C" int sgemm_ex_check_args(int transA, int transB, int M, int N, int K, 
     return SGEMM_OK;
 }
 
+extern "C" int sgemm_ex_ws_check_args(int transA, int transB, int M, int N, int K, float alpha, const float *A,
+                                      int lda, const float *B, int ldb, float beta, const float *C, int ldc,
+                                      const void *workspace, std::size_t workspace_bytes, int variant)
+{
+    const int rc = sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant);
+    if (rc != SGEMM_OK || M == 0 || N == 0) return rc;
+    if (workspace == nullptr || workspace_bytes == 0) return SGEMM_OK;
+    const std::uintptr_t base = reinterpret_cast<std::uintptr_t>(workspace);
+    const Span ws{base, base + workspace_bytes};
+    if (overlap(ws, span_of(C, M, N, ldc))) return SGEMM_ERR_ALIAS;
+    if (K > 0 && alpha != 0.0f) {
+        const bool ta = transA == SGEMM_OP_T, tb = transB == SGEMM_OP_T;
+        if (overlap(ws, span_of(A, ta ? K : M, ta ? M : K, lda)) || overlap(ws, span_of(B, tb ? N : K, tb ? K : N, ldb)))
+            return SGEMM_ERR_ALIAS;
+    }
+    return SGEMM_OK;
+}
+
 extern "C" int sgemm_lp_check_args(int dtype, int transA, int transB, int M, int N, int K, float alpha,
                                    const void *A, int lda, const void *B, int ldb, float beta, const float *C,
                                    int ldc)

@@ -36,6 +36,13 @@ hipError_t launch_mfma_nn(const Problem &p, hipStream_t stream);  // one per tra
 hipError_t launch_mfma_nt(const Problem &p, hipStream_t stream);
 hipError_t launch_mfma_tn(const Problem &p, hipStream_t stream);
 hipError_t launch_mfma_tt(const Problem &p, hipStream_t stream);
+// The matrix-core variant on the split schedule (mfma.hpp): `grid`
+// work-groups with `tile` shapes, partial tiles in `ws` (at least
+// split_workspace_bytes(tile, grid) bytes, select.hpp).
+hipError_t launch_mfma_sk_nn(const Problem &p, MfmaTile tile, float *ws, int grid, hipStream_t stream);
+hipError_t launch_mfma_sk_nt(const Problem &p, MfmaTile tile, float *ws, int grid, hipStream_t stream);
+hipError_t launch_mfma_sk_tn(const Problem &p, MfmaTile tile, float *ws, int grid, hipStream_t stream);
+hipError_t launch_mfma_sk_tt(const Problem &p, MfmaTile tile, float *ws, int grid, hipStream_t stream);
 // C = beta * C over the M x N window (zeros, without reading C, when beta is
 // 0): the whole product when K == 0 or alpha == 0.
 hipError_t launch_scale(const Problem &p, hipStream_t stream);

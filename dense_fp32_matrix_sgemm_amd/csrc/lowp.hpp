@@ -478,14 +478,14 @@ __device__ __forceinline__ unsigned lp_lds_address(const short *p)
 
 // One global_load_lds_dwordx4: lane i copies the 16 bytes at its src to LDS
 // byte address lds + 16 i (lds is wave-uniform; the instruction takes it in
-// M0). Written as inline assembly so that the compiler does not see an LDS
-// store whose completion it would then wait for (with vmcnt(0)) before LDS
-// reads of other stages; the loop's own waits order it.
+// M0, which the compiler loads for the statement as its input operand).
+// Written as inline assembly so that the compiler does not see an LDS store
+// whose completion it would then wait for (with vmcnt(0)) before LDS reads
+// of other stages; the loop's own waits order it.
 __device__ __forceinline__ void lp_dma16(const std::uint16_t *src, unsigned lds)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
-                 "v"(src)
-                 : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %1, off" ::"{m0}"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+                 : "memory");
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier; also a compiler barrier for

@@ -473,9 +473,17 @@ __device__ __forceinline__ void general_tile(const Problem &p, int tm, int tn, f
 //    the partial slab is loaded element by element as before. Stores are
 //    guarded.
 // interior_tile computes the BM x BN tile (tm, tn) of the product p; `lds`
-// holds Tiles<Cfg, TA, TB>::kLdsFloats floats.
-template <class Cfg, bool TA, bool TB, bool EDGE>
-__device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, float *lds)
+// holds Tiles<Cfg, TA, TB>::kLdsFloats floats. With RANGE it sums only the
+// slabs [rg.s_begin, rg.s_end) of K (slab n_full being the partial one, if K
+// is not a multiple of BK) and, when rg.ws is set, stores the unscaled sum
+// row-major into rg.ws (BM x BN floats) instead of updating C.
+struct TileRange {
+    int s_begin, s_end;
+    float *ws;
+};
+
+template <class Cfg, bool TA, bool TB, bool EDGE, bool RANGE = false>
+__device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, float *lds, const TileRange &rg = {})
 {
     using T = Tiles<Cfg, TA, TB>;
     using OpA = typename T::OpA;
@@ -497,6 +505,9 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
     const int wm0 = (wave / Cfg::WAVES_N) * Cfg::WM;
     const int wn0 = (wave % Cfg::WAVES_N) * Cfg::WN;
     const int n_full = p.K / BK;
+    const int s_first = RANGE ? rg.s_begin : 0;                                 // first full slab
+    const int s_stop = RANGE ? (rg.s_end < n_full ? rg.s_end : n_full) : n_full;  // past the last full slab
+    const bool tail = n_full * BK < p.K && (!RANGE || rg.s_end > n_full);         // the partial slab
 
     floatx16 acc[OpA::NB][OpB::NB];
     clear(acc);
@@ -510,8 +521,8 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
     const std::int64_t slab_a = OpA::KC ? BK : BK * p.lda, slab_b = OpB::KC ? BK : BK * p.ldb;
 
     f32x4 ra[CA], rb[CB];
-    auto fetch = [&](int slab) {
-        const std::int64_t ka = slab * slab_a, kb = slab * slab_b;
+    auto fetch = [&](int slab) {  // slab counted from s_first
+        const std::int64_t ka = (s_first + slab) * slab_a, kb = (s_first + slab) * slab_b;
 #pragma unroll
         for (int q = 0; q < CA; ++q)
             ra[q] = load16u(srca.chunk(q) + ka);
@@ -573,7 +584,7 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
         }
     };
 
-    const int n = n_full;
+    const int n = s_stop - s_first;
     if (n > 0) {
         fetch(0);
         stash(0);
@@ -619,7 +630,7 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
         }
         __syncthreads();
     }
-    if (n_full * BK < p.K) {
+    if (tail) {
         // Partial last slab: k >= K reads as zero. Written straight to LDS one
         // element at a time; this runs once.
         const int k0 = n_full * BK;
@@ -644,7 +655,16 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
         multiply(0);
     }
 
-    write_tile<OpA, OpB>(p, acc, m0 + wm0, n0 + wn0, l32, h, !EDGE);
+    if (RANGE && rg.ws != nullptr) {
+        Problem q = p;  // the partial tile, unscaled, all of it
+        q.C = rg.ws;
+        q.ldc = BN;
+        q.alpha = 1.0f;
+        q.beta = 0.0f;
+        write_tile<OpA, OpB>(q, acc, wm0, wn0, l32, h, true);
+    } else {
+        write_tile<OpA, OpB>(p, acc, m0 + wm0, n0 + wn0, l32, h, !EDGE);
+    }
 }
 
 // Tile shapes (tiles.hpp).
@@ -700,6 +720,115 @@ hipError_t launch_tiles(const Problem &p, hipStream_t stream)
         return hipLaunchKernel(kernel, dim3(unsigned(tiles_m) * unsigned(tiles_n)), dim3(Cfg::kThreads), args, 0,
                                stream);
     });
+}
+
+// Split-K over a persistent grid ("stream-K" schedule), for products whose
+// tiles would leave compute units idle or unevenly loaded. The product's
+// work is the sequence of (tile, slab) iterations, tile after tile, each
+// tile's slabs in K order; work-group w (numbered so that each XCD holds a
+// contiguous run) takes iterations [w * per_wg, (w + 1) * per_wg), so every
+// compute unit gets the same amount. A tile whose slabs all fall to one
+// work-group is computed and stored as usual. A tile shared by several is
+// computed in pieces: each work-group stores its unscaled partial tile in
+// the workspace, and a second kernel adds a tile's partials in K order (so
+// the result is the same on every run), scales, and updates C. Work-group w
+// stores at most two partials: slot 2w for the piece its range starts with,
+// slot 2w + 1 for the one it ends with.
+struct SkPlan {
+    int tiles_m, tiles_n;  // tile grid
+    int slabs;             // slabs per tile, the partial one included
+    int per_wg;            // iterations per work-group
+    float *ws;             // 2 * grid partial tiles of BM * BN floats
+};
+
+template <class Cfg, bool TA, bool TB>
+__global__ __launch_bounds__(Cfg::kThreads)
+__attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mfma_sk_kernel(Problem p, SkPlan sk)
+{
+    __shared__ __attribute__((aligned(16))) float lds[Tiles<Cfg, TA, TB>::kLdsFloats];
+    constexpr int BM = Cfg::BM, BN = Cfg::BN;
+    const int w = int(logical_workgroup(blockIdx.x, gridDim.x));
+    const std::int64_t total = std::int64_t(sk.tiles_m) * sk.tiles_n * sk.slabs;
+    const std::int64_t begin = std::int64_t(w) * sk.per_wg;
+    const std::int64_t end = begin + sk.per_wg < total ? begin + sk.per_wg : total;
+    for (std::int64_t it = begin; it < end;) {
+        const std::int64_t t = it / sk.slabs;
+        const int s0 = int(it - t * sk.slabs);
+        const int s1 = end - t * sk.slabs < sk.slabs ? int(end - t * sk.slabs) : sk.slabs;
+        int tm, tn;
+        tile_of_index(unsigned(t), sk.tiles_m, unsigned(sk.tiles_n), Cfg::kGroupM, tm, tn);
+        const bool whole = s0 == 0 && s1 == sk.slabs;
+        const TileRange rg{s0, s1, whole ? nullptr : sk.ws + (2 * std::int64_t(w) + (it == begin ? 0 : 1)) * BM * BN};
+        const bool edge = std::int64_t(tm + 1) * BM > p.M || std::int64_t(tn + 1) * BN > p.N;
+        if (edge)
+            interior_tile<Cfg, TA, TB, true, true>(p, tm, tn, lds, rg);
+        else
+            interior_tile<Cfg, TA, TB, false, true>(p, tm, tn, lds, rg);
+        it = t * sk.slabs + s1;
+        __syncthreads();  // the next piece reuses the LDS buffers
+    }
+}
+
+// C <- alpha * (sum of a shared tile's partials, in K order) + beta * C, four
+// consecutive columns per work-item; tile blockIdx.y (logical numbering).
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void mfma_sk_fixup_kernel(Problem p, SkPlan sk)
+{
+    static_assert(BN % 4 == 0, "four columns per work-item");
+    const int t = blockIdx.y;
+    const std::int64_t first = std::int64_t(t) * sk.slabs, last = first + sk.slabs - 1;
+    const int w0 = int(first / sk.per_wg), w1 = int(last / sk.per_wg);
+    if (w0 == w1) return;  // stored whole by its work-group
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= BM * BN) return;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int w = w0; w <= w1; ++w) {
+        const std::int64_t slot = 2 * std::int64_t(w) + (std::int64_t(w) * sk.per_wg >= first ? 0 : 1);
+        v += *reinterpret_cast<const f32x4 *>(sk.ws + slot * BM * BN + e);
+    }
+    int tm, tn;
+    tile_of_index(unsigned(t), sk.tiles_m, unsigned(sk.tiles_n), SGEMM_MFMA_GROUP_M, tm, tn);
+    const std::int64_t row = std::int64_t(tm) * BM + e / BN;
+    const int col = tn * BN + e % BN;
+    const float vals[4] = {v[0], v[1], v[2], v[3]};
+    const bool inside = row < p.M && col + 4 <= p.N;
+    update_n<4>(p.C, p.ldc, row, col, p.M, p.N, vals, inside, p.alpha, p.beta);
+}
+
+// Workspace bytes the split schedule of this configuration needs with `grid`
+// work-groups.
+template <class Cfg>
+constexpr std::size_t sk_workspace_bytes(int grid)
+{
+    return std::size_t(2) * std::size_t(grid) * Cfg::BM * Cfg::BN * sizeof(float);
+}
+
+template <class Cfg, bool TA, bool TB>
+hipError_t launch_sk(const Problem &p, float *ws, int grid, hipStream_t stream)
+{
+    SkPlan sk;
+    sk.tiles_m = int((std::int64_t(p.M) + Cfg::BM - 1) / Cfg::BM);
+    sk.tiles_n = int((std::int64_t(p.N) + Cfg::BN - 1) / Cfg::BN);
+    sk.slabs = int((std::int64_t(p.K) + Cfg::BK - 1) / Cfg::BK);
+    const std::int64_t total = std::int64_t(sk.tiles_m) * sk.tiles_n * sk.slabs;
+    sk.per_wg = int((total + grid - 1) / grid);
+    sk.ws = ws;
+    Problem q = p;
+    void *args[] = {&q, &sk};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&mfma_sk_kernel<Cfg, TA, TB>), dim3(grid),
+                                   dim3(Cfg::kThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+    const unsigned per_tile = unsigned((Cfg::BM * Cfg::BN / 4 + 255) / 256);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&mfma_sk_fixup_kernel<Cfg::BM, Cfg::BN>),
+                           dim3(per_tile, unsigned(sk.tiles_m * sk.tiles_n)), dim3(256), args, 0, stream);
+}
+
+// The split schedule with the tile shape the host chose.
+template <bool TA, bool TB>
+hipError_t launch_sk_by_tile(const Problem &p, MfmaTile tile, float *ws, int grid, hipStream_t stream)
+{
+    if (tile == MfmaTile::Mid) return launch_sk<MidCfg, TA, TB>(p, ws, grid, stream);
+    return launch_sk<BigCfg, TA, TB>(p, ws, grid, stream);
 }
 
 // One launch with the tile shape the host chose for this product

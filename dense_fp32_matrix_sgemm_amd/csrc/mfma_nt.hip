@@ -9,4 +9,9 @@ hipError_t launch_mfma_nt(const Problem &p, hipStream_t stream)
     return launch_by_shape<false, true>(p, stream);
 }
 
+hipError_t launch_mfma_sk_nt(const Problem &p, MfmaTile tile, float *ws, int grid, hipStream_t stream)
+{
+    return launch_sk_by_tile<false, true>(p, tile, ws, grid, stream);
+}
+
 }  // namespace sgemm_impl

@@ -16,6 +16,7 @@
 // (A 256x128 shape measured 0.85-0.94 alone and never beat these three.)
 //
 // Pure C++ (no HIP), so it is tested on the host.
+#include <cstddef>
 #include <cstdint>
 
 #include "select.hpp"
@@ -43,24 +44,104 @@ double launch_time(const Candidate &c, std::int64_t M, std::int64_t N, std::int6
     return t;
 }
 
+const Candidate kCandidates[] = {
+    {MfmaTile::Big, tiles::kBig[0], tiles::kBig[1], 1, {1.0, 0, 0, 0}},
+    {MfmaTile::Mid, tiles::kMid[0], tiles::kMid[1], 2, {0.88, 0.93, 0, 0}},
+    {MfmaTile::Small, tiles::kSmall[0], tiles::kSmall[1], 4, {0.59, 0.72, 0.79, 0.84}},
+};
+
 }  // namespace
 
 MfmaTile choose_mfma_tile(int M, int N, int cus)
 {
-    using namespace tiles;
-    const Candidate cands[] = {
-        {MfmaTile::Big, kBig[0], kBig[1], 1, {1.0, 0, 0, 0}},
-        {MfmaTile::Mid, kMid[0], kMid[1], 2, {0.88, 0.93, 0, 0}},
-        {MfmaTile::Small, kSmall[0], kSmall[1], 4, {0.59, 0.72, 0.79, 0.84}},
-    };
     const std::int64_t n_cus = cus > 0 ? cus : 256;
     MfmaTile best = MfmaTile::Big;
     double best_t = -1.0;
-    for (const Candidate &c : cands) {  // ties go to the larger tile (less traffic)
+    for (const Candidate &c : kCandidates) {  // ties go to the larger tile (less traffic)
         const double t = launch_time(c, M, N, n_cus);
         if (best_t < 0.0 || t < best_t) {
             best_t = t;
             best = c.tile;
+        }
+    }
+    return best;
+}
+
+// Split schedule. Times in seconds, from the same measured rates: rate 1 is
+// 147 TFLOP/s over 256 compute units. Work-group w of `grid` takes
+// ceil(tiles * slabs / grid) iterations of BM x BN x BK; a compute unit
+// runs `slots` work-groups at once at `rate`. Tiles shared by several
+// work-groups cost their partials' round trip (written, then read by the
+// second kernel) and that kernel's launch. The rates and the partials'
+// bandwidth (they mostly stay in the 256 MB Infinity Cache) are fitted to
+// forced-schedule runs on MI355X: 256x256 pieces 0.93, 128x128 pieces two at
+// a time 0.85 (3001 x 2047 x 4093, 3072 x 2048 x 4096, 2560^3, 1536^3).
+namespace {
+
+constexpr double kRate1PerCu = 147e12 / 256;  // FLOP/s of one compute unit at rate 1
+constexpr double kPartialBytesPerS = 8e12;    // the partials' write and read
+constexpr double kSecondLaunchS = 4e-6;       // the adding kernel's launch and ramp
+
+struct SplitCandidate {
+    MfmaTile tile;
+    int bm, bn, bk;
+    int slots;
+    double rate;
+};
+
+double split_time(const SplitCandidate &c, std::int64_t M, std::int64_t N, std::int64_t K, int cus, int grid)
+{
+    const std::int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    const std::int64_t slabs = ceil_div(K, c.bk);
+    const std::int64_t per_wg = ceil_div(tiles * slabs, grid);
+    const double wg_flop = double(per_wg) * c.bm * c.bn * c.bk * 2.0;
+    double t = double(c.slots) * wg_flop / (kRate1PerCu * c.rate);
+    (void)cus;
+    // Pieces of shared tiles: tile t spans work-groups [t*slabs/per_wg, ((t+1)*slabs-1)/per_wg].
+    std::int64_t pieces = 0;
+    for (std::int64_t t0 = 0; t0 < tiles; ++t0) {
+        const std::int64_t w0 = (t0 * slabs) / per_wg, w1 = ((t0 + 1) * slabs - 1) / per_wg;
+        if (w1 > w0) pieces += w1 - w0 + 1;
+    }
+    if (pieces > 0) t += 2.0 * double(pieces) * c.bm * c.bn * 4.0 / kPartialBytesPerS + kSecondLaunchS;
+    return t;
+}
+
+}  // namespace
+
+std::size_t split_workspace_bytes(MfmaTile tile, int grid)
+{
+    const int *d = tile == MfmaTile::Mid ? tiles::kMid : tiles::kBig;
+    return std::size_t(2) * std::size_t(grid > 0 ? grid : 0) * std::size_t(d[0]) * std::size_t(d[1]) * sizeof(float);
+}
+
+SplitChoice choose_split(int M, int N, int K, int cus)
+{
+    using namespace tiles;
+    SplitChoice none{false, MfmaTile::Big, 0, 0};
+    if (M <= 0 || N <= 0 || K <= 0) return none;
+    const int n_cus = cus > 0 ? cus : 256;
+    // Whole tiles: the chosen shape's estimated time.
+    const MfmaTile dp_tile = choose_mfma_tile(M, N, n_cus);
+    const Candidate *dp = &kCandidates[0];
+    for (const Candidate &c : kCandidates)
+        if (c.tile == dp_tile) dp = &c;
+    const double t_dp = launch_time(*dp, M, N, n_cus) * 2.0 * double(K) / kRate1PerCu;
+
+    const SplitCandidate splits[] = {
+        {MfmaTile::Big, kBig[0], kBig[1], kBig[2], 1, 0.93},
+        {MfmaTile::Mid, kMid[0], kMid[1], kMid[2], 2, 0.85},
+    };
+    SplitChoice best = none;
+    double best_t = 0.97 * t_dp;  // the split schedule must win by a margin
+    for (const SplitCandidate &c : splits) {
+        const int grid = n_cus * c.slots;
+        const std::int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+        if (tiles > 65535) continue;  // the adding kernel's grid rows
+        const double t = split_time(c, M, N, K, n_cus, grid);
+        if (t < best_t) {
+            best_t = t;
+            best = {true, c.tile, grid, split_workspace_bytes(c.tile, grid)};
         }
     }
     return best;
@@ -82,4 +163,16 @@ extern "C" int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN)
     *BM = dims[0];
     *BN = dims[1];
     return SGEMM_OK;
+}
+
+extern "C" std::size_t sgemm_ex_workspace_size(int transA, int transB, int M, int N, int K, int cus)
+{
+    using namespace sgemm_impl;
+    const bool ok_op = (transA == SGEMM_OP_N || transA == SGEMM_OP_T) && (transB == SGEMM_OP_N || transB == SGEMM_OP_T);
+    if (!ok_op || M <= 0 || N <= 0 || K <= 0) return 0;
+    // Products whose free-index-contiguous operand is under 4 wide take the
+    // general tiles, never the split schedule.
+    if ((transA == SGEMM_OP_T && M < 4) || (transB == SGEMM_OP_N && N < 4)) return 0;
+    const SplitChoice c = choose_split(M, N, K, cus);
+    return c.use ? c.bytes : 0;
 }

@@ -1,6 +1,8 @@
 // Host-side choice of the matrix-core launch shape (pure C++).
 #pragma once
 
+#include <cstddef>
+
 #include "tiles.hpp"
 
 namespace sgemm_impl {
@@ -8,5 +10,19 @@ namespace sgemm_impl {
 // The interior tile shape with the smallest estimated time for an M x N
 // product on `cus` compute units (cus <= 0 means 256, an MI355X).
 MfmaTile choose_mfma_tile(int M, int N, int cus);
+
+// The split ("stream-K") schedule for an M x N x K product: whether its
+// estimated time beats the whole-tile launch, the tile shape and work-group
+// count it would use, and the workspace it needs then (0 when not used).
+struct SplitChoice {
+    bool use;
+    MfmaTile tile;
+    int grid;
+    std::size_t bytes;
+};
+SplitChoice choose_split(int M, int N, int K, int cus);
+
+// Workspace of the split schedule: two partial tiles per work-group.
+std::size_t split_workspace_bytes(MfmaTile tile, int grid);
 
 }  // namespace sgemm_impl

@@ -147,21 +147,31 @@ __device__ __forceinline__ void update_n(float *base, std::int64_t ld, std::int6
 // column by column inside a band, so that the tiles resident on one XCD at a
 // time share a few row panels of A and column panels of B in its L2.
 // Both steps are bijections on [0, tiles_m * tiles_n).
-__device__ __forceinline__ void tile_of_workgroup(unsigned w, unsigned n_wg, int tiles_m, int group_m, int &tm,
-                                                  int &tn)
+__device__ __forceinline__ unsigned logical_workgroup(unsigned w, unsigned n_wg)
 {
     constexpr unsigned kXcds = 8;
     const unsigned q = n_wg / kXcds, r = n_wg % kXcds;
     const unsigned xcd = w % kXcds, idx = w / kXcds;
-    const unsigned logical = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
 
-    const unsigned tiles_n = n_wg / unsigned(tiles_m);
+// Logical tile number -> (tm, tn), in bands of group_m tile rows walked
+// column by column (the second step above).
+__device__ __forceinline__ void tile_of_index(unsigned logical, int tiles_m, unsigned tiles_n, int group_m, int &tm,
+                                              int &tn)
+{
     const unsigned band = unsigned(group_m) * tiles_n;
     const unsigned first_m = (logical / band) * unsigned(group_m);
     const unsigned rows_in_band = min(unsigned(tiles_m) - first_m, unsigned(group_m));
     const unsigned in_band = logical % band;
     tm = int(first_m + in_band % rows_in_band);
     tn = int(in_band / rows_in_band);
+}
+
+__device__ __forceinline__ void tile_of_workgroup(unsigned w, unsigned n_wg, int tiles_m, int group_m, int &tm,
+                                                  int &tn)
+{
+    tile_of_index(logical_workgroup(w, n_wg), tiles_m, n_wg / unsigned(tiles_m), group_m, tm, tn);
 }
 
 }  // namespace sgemm_impl

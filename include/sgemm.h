@@ -29,6 +29,8 @@
 #ifndef SGEMM_H
 #define SGEMM_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -179,6 +181,63 @@ int sgemm_ex_check_args(int transA, int transB, int M, int N, int K,
                         float beta,
                         const float *C, int ldc,
                         int variant);
+
+/*
+ * sgemm_ex with a device workspace, so that the matrix-core variant can run
+ * products whose tiles would load the compute units unevenly on a split
+ * schedule. Tiles are tuned per problem as section 07 and exercise 2 of
+ * "Matrix Multiplication -- Naive to Tiled" describe; splitting a tile's K
+ * range over several work-groups is this library's addition to that.
+ *
+ * Split schedule: the product's (tile, K slab) iterations, tile after tile,
+ * are dealt out in equal runs to one work-group per compute unit (two with
+ * 128 x 128 tiles). A tile whose slabs all fall to one work-group is
+ * computed and stored as in sgemm_ex; a tile shared by several is computed
+ * in pieces whose unscaled sums go to the workspace, and a second kernel adds
+ * each shared tile's pieces in K order and applies alpha and beta. The result
+ * is therefore the same on every run, and within the bound sgemm_ex states
+ * (its last bits may differ from sgemm_ex's, whose sums are not split).
+ *
+ * Arguments: those of sgemm_ex, plus
+ *   workspace        device memory the call may use (contents undefined
+ *                    afterwards; the caller owns it); NULL, or
+ *   workspace_bytes  smaller than sgemm_ex_workspace_size() for this product,
+ *                    makes the call exactly sgemm_ex.
+ * The library decides per product whether the split schedule is faster; only
+ * the matrix-core variant (and SGEMM_BEST) uses it. Calls that share a
+ * workspace must be ordered on one stream: concurrent calls race on it.
+ *
+ * Behaviour: as sgemm_ex, with one more check after sgemm_ex's: a non-empty
+ * workspace that overlaps C, or A or B when they are read, is SGEMM_ERR_ALIAS.
+ * Returns SGEMM_OK or a negative sgemm_status.
+ */
+int sgemm_ex_ws(int transA, int transB, int M, int N, int K,
+                float alpha,
+                const float *A, int lda,
+                const float *B, int ldb,
+                float beta,
+                float *C, int ldc,
+                void *workspace, size_t workspace_bytes,
+                void *stream, int variant);
+
+/* The host-side argument checks of sgemm_ex_ws() alone (same codes, same
+ * order); makes no HIP call and touches no memory. */
+int sgemm_ex_ws_check_args(int transA, int transB, int M, int N, int K,
+                           float alpha,
+                           const float *A, int lda,
+                           const float *B, int ldb,
+                           float beta,
+                           const float *C, int ldc,
+                           const void *workspace, size_t workspace_bytes,
+                           int variant);
+
+/*
+ * Workspace bytes sgemm_ex_ws needs to run this product on the split
+ * schedule on a device with `cus` compute units (cus <= 0: 256, an MI355X),
+ * or 0 when it would not split it (the whole-tile schedule is estimated to
+ * be as fast, or the arguments are invalid). Pure host logic: no HIP call.
+ */
+size_t sgemm_ex_workspace_size(int transA, int transB, int M, int N, int K, int cus);
 
 /*
  * The reduced-precision workload: the tensor-core variant "Matrix

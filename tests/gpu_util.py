@@ -56,14 +56,15 @@ def gemm(A: np.ndarray, B: np.ndarray, variant, ld_pad=(0, 0, 0), offset=(0, 0, 
 
 def gemm_ex(transA: bool, transB: bool, alpha: float, A: np.ndarray, B: np.ndarray, beta: float,
             C0: np.ndarray, variant, ld_pad=(0, 0, 0), offset=(0, 0, 0), stream=None,
-            return_buffer=False, fill=float("nan")):
+            return_buffer=False, fill=float("nan"), workspace=None):
     """Run sgemm_ex on copies of the stored operands A, B and the initial C0
     (M x N); returns the updated C (numpy float32).
 
     A is stored M x K (K x M when transA), B K x N (N x K when transB). The
     padding of every buffer holds ``fill`` (NaN: it must never be read), and
     with ``return_buffer`` the whole backing buffer of C and its (ld, offset)
-    come back too.
+    come back too. With ``workspace`` (a device tensor) the call is
+    sgemm_ex_ws with that workspace.
     """
     M, N = C0.shape
     K = A.shape[0] if transA else A.shape[1]
@@ -72,10 +73,15 @@ def gemm_ex(transA: bool, transB: bool, alpha: float, A: np.ndarray, B: np.ndarr
     dB, _ = device_matrix(B, ldb, offset[1], fill)
     dC, cbuf = device_matrix(C0, ldc, offset[2], fill=SENTINEL)
     s = stream or torch.cuda.current_stream()
-    rc = sg.sgemm_ex(sg.SGEMM_OP_T if transA else sg.SGEMM_OP_N, sg.SGEMM_OP_T if transB else sg.SGEMM_OP_N,
-                     M, N, K, alpha, dA.data_ptr(), max(lda, 1), dB.data_ptr(), max(ldb, 1), beta,
-                     dC.data_ptr(), max(ldc, 1), s.cuda_stream,
-                     sg.VARIANTS[variant] if isinstance(variant, str) else variant)
+    ta, tb = sg.SGEMM_OP_T if transA else sg.SGEMM_OP_N, sg.SGEMM_OP_T if transB else sg.SGEMM_OP_N
+    v = sg.VARIANTS[variant] if isinstance(variant, str) else variant
+    if workspace is None:
+        rc = sg.sgemm_ex(ta, tb, M, N, K, alpha, dA.data_ptr(), max(lda, 1), dB.data_ptr(), max(ldb, 1), beta,
+                         dC.data_ptr(), max(ldc, 1), s.cuda_stream, v)
+    else:
+        rc = sg.sgemm_ex_ws(ta, tb, M, N, K, alpha, dA.data_ptr(), max(lda, 1), dB.data_ptr(), max(ldb, 1), beta,
+                            dC.data_ptr(), max(ldc, 1), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), s.cuda_stream, v)
     if rc != sg.SGEMM_OK:
         raise sg.SgemmError(rc)
     s.synchronize()

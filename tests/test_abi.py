@@ -260,3 +260,65 @@ def test_lp_no_device_is_reported_not_crashed(lib):
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert sg.sgemm_lp(BF, N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, None) == sg.SGEMM_ERR_DEVICE
     assert sg.sgemm_lp(F16, N_, N_, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, C, 4, None) == sg.SGEMM_OK
+
+
+WS = 0x7000_0000   # a fake workspace address, far from A, B and C
+
+WS_CASES = [
+    # (transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, bytes, variant) -> status
+    # sgemm_ex's checks come first, in its order.
+    ((2, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, WS, 64, 0), sg.SGEMM_ERR_OP),
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, A, 64, 9), sg.SGEMM_ERR_VARIANT),
+    ((N_, N_, 4, 4, 4, 1.0, None, 4, B, 4, 0.0, C, 4, WS, 64, 0), sg.SGEMM_ERR_NULL),
+    # Then the workspace, when it is non-empty: it must not overlap C, or A and
+    # B when they are read.
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, WS, 64, 0), sg.SGEMM_OK),
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, None, 0, 0), sg.SGEMM_OK),
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, A, 0, 0), sg.SGEMM_OK),       # empty: never used
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, C + 4 * 15, 4, 0), sg.SGEMM_ERR_ALIAS),
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, C + 4 * 16, 4, 0), sg.SGEMM_OK),
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, C - 4, 4, 0), sg.SGEMM_OK),    # ends where C starts
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, C - 4, 5, 0), sg.SGEMM_ERR_ALIAS),
+    ((T_, N_, 2, 4, 8, 1.0, A, 2, B, 4, 0.0, C, 4, A + 4 * 15, 4, 0), sg.SGEMM_ERR_ALIAS),   # A^T: 16 floats
+    ((T_, N_, 2, 4, 8, 1.0, A, 2, B, 4, 0.0, C, 4, A + 4 * 16, 4, 0), sg.SGEMM_OK),
+    ((N_, N_, 4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, B + 8, 4, 0), sg.SGEMM_ERR_ALIAS),
+    ((N_, N_, 4, 4, 4, 0.0, A, 4, B, 4, 2.0, C, 4, B + 8, 4, 0), sg.SGEMM_OK),    # alpha 0: B not read
+    ((N_, N_, 0, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, C, 64, 0), sg.SGEMM_OK),       # empty C: nothing checked
+]
+
+
+@pytest.mark.parametrize("args,want", WS_CASES)
+def test_ws_check_args(lib, args, want):
+    assert sg.sgemm_ex_ws_check_args(*args) == want
+
+
+@pytest.mark.parametrize("args,want", [c for c in WS_CASES if c[1] != sg.SGEMM_OK])
+def test_ws_rejects_before_touching_the_gpu(lib, args, want):
+    *head, ws, nbytes, variant = args
+    assert sg.sgemm_ex_ws(*head, ws, nbytes, None, variant) == want
+
+
+def test_ws_nothing_to_do_returns_ok_without_gpu(lib):
+    assert sg.sgemm_ex_ws(N_, N_, 0, 5, 5, 1.0, None, 5, None, 5, 0.0, None, 5, WS, 64, None, 3) == sg.SGEMM_OK
+    assert sg.sgemm_ex_ws(T_, N_, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, C, 4, WS, 64, None, 3) == sg.SGEMM_OK
+
+
+def test_split_workspace_size(lib):
+    # Uneven tile loads take the split schedule: two partial tiles per
+    # work-group, one 256x256 work-group per compute unit or two 128x128.
+    big, mid = 2 * 256 * 256 * 256 * 4, 2 * 512 * 128 * 128 * 4
+    assert sg.sgemm_ex_workspace_size(N_, N_, 3001, 2047, 4093, 256) == big
+    assert sg.sgemm_ex_workspace_size(T_, T_, 3072, 2048, 4096, 0) == big
+    assert sg.sgemm_ex_workspace_size(N_, T_, 512, 512, 16384, 256) == mid
+    for cus in (64, 128, 304):   # sized for the device's compute units when used
+        assert sg.sgemm_ex_workspace_size(N_, N_, 3001, 2047, 4093, cus) in (0, 2 * cus * 256 * 256 * 4,
+                                                                              2 * 2 * cus * 128 * 128 * 4)
+    # Products that whole tiles already spread evenly keep them.
+    for shape in [(4096, 4096, 4096), (8192, 8192, 8192), (2048, 2048, 2048), (1024, 1024, 1024), (128, 128, 128)]:
+        assert sg.sgemm_ex_workspace_size(N_, N_, *shape, 256) == 0, shape
+    # Invalid or empty products, and operands too narrow for the fast tiles.
+    assert sg.sgemm_ex_workspace_size(2, N_, 3001, 2047, 4093, 256) == 0
+    assert sg.sgemm_ex_workspace_size(N_, N_, -1, 2047, 4093, 256) == 0
+    assert sg.sgemm_ex_workspace_size(N_, N_, 3001, 2047, 0, 256) == 0
+    assert sg.sgemm_ex_workspace_size(N_, N_, 4096, 3, 1 << 20, 256) == 0
+    assert sg.sgemm_ex_workspace_size(T_, T_, 3, 4096, 1 << 20, 256) == 0

@@ -110,3 +110,55 @@ def test_two_streams_at_once():
     for A, B, _, _, dC in cases:
         Cref, S = oracle.gemm(A, B, with_abs=True)
         assert_within(dC.cpu().numpy(), Cref, S, "two streams")
+
+
+def test_split_schedule_under_graph_capture():
+    # sgemm_ex_ws on the split schedule (two kernels and the workspace, no
+    # allocation and no memset) captured once and replayed on new inputs.
+    print("[graphs] split schedule capture and replay", flush=True)
+    dev = torch.device("cuda:0")
+    M, N, K = 1000, 1000, 8000
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    need = sg.sgemm_ex_workspace_size(sg.SGEMM_OP_N, sg.SGEMM_OP_N, M, N, K, cus)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    dA = torch.empty((M, K), device=dev)
+    dB = torch.empty((K, N), device=dev)
+    dC = torch.empty((M, N), device=dev)
+    rng = np.random.default_rng(7)
+    rows, cols = rng.integers(0, M, 2000), rng.integers(0, N, 2000)
+
+    def load(seed):
+        A, B = synth.operands(M, N, K, "pm1", seed_a=seed, seed_b=seed + 1)
+        C0 = synth.uniform_pm1(seed + 2, (M, N))
+        dA.copy_(torch.from_numpy(A))
+        dB.copy_(torch.from_numpy(B))
+        dC.copy_(torch.from_numpy(C0))
+        return A, B, C0
+
+    def check(data, what):
+        A, B, C0 = data
+        want, S = oracle.gemm_ex_entries(False, False, 1.5, A, B, -0.5, C0, rows, cols)
+        assert_within(dC.cpu().numpy()[rows, cols], want, S, what)
+
+    side = torch.cuda.Stream()
+    data = load(60)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        sg.gemm(dA, dB, dC, alpha=1.5, beta=-0.5, workspace=ws)
+    torch.cuda.synchronize()
+    check(data, "eager")
+    graph = torch.cuda.CUDAGraph()
+    load(70)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        sg.gemm(dA, dB, dC, alpha=1.5, beta=-0.5, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        data = load(80 + 10 * rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        check(data, f"replay {rep}")
+        torch.matmul(dA, dB).sum().item()   # eager work between replays
+    del graph
