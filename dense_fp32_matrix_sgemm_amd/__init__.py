@@ -71,7 +71,7 @@ VARIANTS = {"best": SGEMM_BEST, "naive": SGEMM_NAIVE, "tiled": SGEMM_TILED,
 # Symbols the shared library exports (the functions of include/sgemm.h).
 EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args", "sgemm_ex_ws", "sgemm_ex_ws_check_args",
            "sgemm_ex_workspace_size", "sgemm_lp", "sgemm_lp_check_args", "sgemm_status_string", "sgemm_variant_name",
-           "sgemm_best_variant", "sgemm_mfma_tile")
+           "sgemm_best_variant", "sgemm_mfma_tile", "sgemm_mfma_shape")
 
 _lib = None
 
@@ -125,6 +125,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int)
     lib.sgemm_mfma_tile.argtypes = [i, i, i, ip, ip]
     lib.sgemm_mfma_tile.restype = i
+    lib.sgemm_mfma_shape.argtypes = [i, i, i, ip]
+    lib.sgemm_mfma_shape.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -184,6 +186,15 @@ def sgemm_variant_name(variant: int):
 
 def sgemm_best_variant(M: int, N: int, K: int) -> int:
     return load_library().sgemm_best_variant(M, N, K)
+
+
+def sgemm_mfma_shape(M: int, N: int, cus: int = 0):
+    """(BM, BN, BK, waves along M, waves along N, k sets) of the MFMA kernel for an M x N product."""
+    shape = (ctypes.c_int * 6)()
+    rc = load_library().sgemm_mfma_shape(M, N, cus, shape)
+    if rc != SGEMM_OK:
+        raise SgemmError(rc)
+    return tuple(shape)
 
 
 def sgemm_mfma_tile(M: int, N: int, cus: int = 0):

@@ -667,11 +667,160 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
     }
 }
 
+// A tile computed by KGROUPS sets of WAVES_M x WAVES_N waves, set g taking
+// its own share (BK / 8 / KGROUPS groups of 8 k) of every slab; the sets'
+// partial tiles are summed at the end. For products with one small tile per
+// compute unit, this puts KGROUPS waves on each SIMD instead of one.
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KGROUPS_>
+struct KSplitConfig {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KGROUPS = KGROUPS_;
+    static constexpr int kThreads = 64 * WAVES_M * WAVES_N * KGROUPS;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    static constexpr int kGroupM = SGEMM_MFMA_GROUP_M;
+    static constexpr int kAccRegs = (WM / 32) * (WN / 32) * 16;
+    static constexpr int kWavesPerEU = kAccRegs >= 128 ? 2 : 4;
+    static constexpr int kGroupsPerWave = BK / 8 / KGROUPS;
+    static_assert(KGROUPS == 2, "the two partial tiles are summed pairwise");
+    static_assert(kGroupsPerWave >= 1 && kGroupsPerWave * 8 * KGROUPS == BK, "whole groups of 8 per set");
+};
+
+template <class Cfg, bool TA, bool TB, bool EDGE>
+__device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, float *lds)
+{
+    using T = Tiles<Cfg, TA, TB>;
+    using OpA = typename T::OpA;
+    using OpB = typename T::OpB;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::kThreads;
+    constexpr int GW = Cfg::kGroupsPerWave;
+    constexpr int CA = OpA::kChunks, CB = OpB::kChunks;
+    constexpr int NS = Cfg::WAVES_M * Cfg::WAVES_N;  // waves per set
+
+    float(*As)[OpA::kFloats] = reinterpret_cast<float(*)[OpA::kFloats]>(lds);
+    float(*Bs)[OpB::kFloats] = reinterpret_cast<float(*)[OpB::kFloats]>(lds + 2 * OpA::kFloats);
+
+    const std::int64_t m0 = std::int64_t(tm) * BM;
+    const int n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid % 64;
+    const int l32 = lane % 32, h = lane / 32;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int set = wave / NS, sw = wave % NS;
+    const int wm0 = (sw / Cfg::WAVES_N) * Cfg::WM;
+    const int wn0 = (sw % Cfg::WAVES_N) * Cfg::WN;
+    const int g0 = set * GW;
+    const int n_full = p.K / BK;
+
+    floatx16 acc[OpA::NB][OpB::NB];
+    clear(acc);
+
+    const OperandSource<OpA, EDGE> srca(p.A, p.lda, m0, p.M, tid);
+    const OperandSource<OpB, EDGE> srcb(p.B, p.ldb, n0, p.N, tid);
+    const std::int64_t slab_a = OpA::KC ? BK : BK * p.lda, slab_b = OpB::KC ? BK : BK * p.ldb;
+
+    f32x4 ra[CA], rb[CB];
+    auto fetch = [&](int slab) {
+        const std::int64_t ka = slab * slab_a, kb = slab * slab_b;
+#pragma unroll
+        for (int q = 0; q < CA; ++q)
+            ra[q] = load16u(srca.chunk(q) + ka);
+#pragma unroll
+        for (int q = 0; q < CB; ++q)
+            rb[q] = load16u(srcb.chunk(q) + kb);
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < CA; ++q)
+            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[q]);
+#pragma unroll
+        for (int q = 0; q < CB; ++q)
+            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[q]);
+    };
+    typename OpA::Frag fa[2];
+    typename OpB::Frag fb[2];
+    auto read_frags = [&](int buf, int g, int slot) {
+        OpA::read(fa[slot], As[buf], wm0, g, l32, h);
+        OpB::read(fb[slot], Bs[buf], wn0, g, l32, h);
+    };
+    auto mfmas = [&](int slot) { mfma_group<OpA, OpB>(acc, fa[slot], fb[slot]); };
+    // This set's groups of one buffer whose first group is already read.
+    auto multiply_mine = [&](int buf) {
+#pragma unroll
+        for (int gg = 0; gg < GW; ++gg) {
+            if (gg + 1 < GW) read_frags(buf, g0 + gg + 1, (gg + 1) & 1);
+            mfmas(gg & 1);
+        }
+    };
+
+    const int n = n_full;
+    if (n > 0) {
+        fetch(0);
+        stash(0);
+        if (n > 1) fetch(1);
+        __syncthreads();
+        read_frags(0, g0, 0);
+        for (int t = 0; t < n; ++t) {
+            const int cur = t & 1;
+            if (t + 1 < n) stash(cur ^ 1);
+            if (t + 2 < n) fetch(t + 2);
+            multiply_mine(cur);
+            __syncthreads();
+            if (t + 1 < n) read_frags(cur ^ 1, g0, 0);
+        }
+    }
+    if (n_full * BK < p.K) {
+        const int k0 = n_full * BK;
+        auto partial = [&](auto op, const float *X, std::int64_t ld, std::int64_t f0, std::int64_t extent,
+                           float *dst) {
+            using Op = decltype(op);
+#pragma unroll 1
+            for (int e = tid; e < Op::kRows * Op::kRowLen; e += NT) {
+                const int r = e / Op::kRowLen, c = e % Op::kRowLen;
+                const int k = Op::KC ? c : r;
+                const std::int64_t f = f0 + (Op::KC ? r : c);
+                const std::int64_t fc = f < extent ? f : extent - 1;
+                const std::int64_t at = Op::KC ? fc * ld + k0 + k : std::int64_t(k0 + k) * ld + fc;
+                dst[r * Op::kPitch + c] = k0 + k < p.K ? X[at] : 0.0f;
+            }
+        };
+        partial(OpA{}, p.A, p.lda, m0, p.M, As[0]);
+        partial(OpB{}, p.B, p.ldb, n0, p.N, Bs[0]);
+        __syncthreads();
+        read_frags(0, g0, 0);
+        multiply_mine(0);
+        __syncthreads();
+    }
+
+    // Set 1's partial tile through LDS into set 0's: register r of lane l of
+    // block (a, b) of spatial wave sw at red[((sw * NA + a) * NB + b) * 16 + r) * 64 + l].
+    constexpr int NA = OpA::NB, NBb = OpB::NB;
+    float *red = lds;
+    if (set == 1) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int b = 0; b < NBb; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[(((sw * NA + a) * NBb + b) * 16 + r) * 64 + lane] = acc[a][b][r];
+    }
+    __syncthreads();
+    if (set == 0) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int b = 0; b < NBb; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[a][b][r] += red[(((sw * NA + a) * NBb + b) * 16 + r) * 64 + lane];
+        write_tile<OpA, OpB>(p, acc, m0 + wm0, n0 + wn0, l32, h, !EDGE);
+    }
+}
+
 // Tile shapes (tiles.hpp).
 using GeneralCfg = MfmaConfig<SGEMM_MFMA_TILE>;
 using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
 using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
 using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
+using KSplitCfg = KSplitConfig<SGEMM_MFMA_KSPLIT_TILE>;
 
 // Products too small for a single interior tile: general tiles only.
 template <class Cfg, bool TA, bool TB, bool VEC>
@@ -697,6 +846,33 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mf
         interior_tile<Cfg, TA, TB, true>(p, tm, tn, lds);
     else
         interior_tile<Cfg, TA, TB, false>(p, tm, tn, lds);
+}
+
+template <class Cfg, bool TA, bool TB>
+__global__ __launch_bounds__(Cfg::kThreads)
+__attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void mfma_ksplit_kernel(Problem p, int tiles_m)
+{
+    constexpr int kPipe = Tiles<Cfg, TA, TB>::kLdsFloats;
+    constexpr int kRed = Cfg::WAVES_M * Cfg::WAVES_N * (Cfg::WM / 32) * (Cfg::WN / 32) * 16 * 64;
+    __shared__ __attribute__((aligned(16))) float lds[kPipe > kRed ? kPipe : kRed];
+    int tm, tn;
+    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, Cfg::kGroupM, tm, tn);
+    const bool edge = std::int64_t(tm + 1) * Cfg::BM > p.M || std::int64_t(tn + 1) * Cfg::BN > p.N;
+    if (edge)
+        ksplit_tile<Cfg, TA, TB, true>(p, tm, tn, lds);
+    else
+        ksplit_tile<Cfg, TA, TB, false>(p, tm, tn, lds);
+}
+
+template <class Cfg, bool TA, bool TB>
+hipError_t launch_ksplit(const Problem &p, hipStream_t stream)
+{
+    const void *kernel = reinterpret_cast<const void *>(&mfma_ksplit_kernel<Cfg, TA, TB>);
+    return for_each_band<Cfg::BM, Cfg::BN>(p, [&](Problem q, int tiles_m, int tiles_n) {
+        void *args[] = {&q, &tiles_m};
+        return hipLaunchKernel(kernel, dim3(unsigned(tiles_m) * unsigned(tiles_n)), dim3(Cfg::kThreads), args, 0,
+                               stream);
+    });
 }
 
 template <class Cfg, bool TA, bool TB>
@@ -842,6 +1018,7 @@ hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
     switch (p.tile) {
     case MfmaTile::Big: return launch_tiles<BigCfg, TA, TB>(p, stream);
     case MfmaTile::Mid: return launch_tiles<MidCfg, TA, TB>(p, stream);
+    case MfmaTile::KSplit: return launch_ksplit<KSplitCfg, TA, TB>(p, stream);
     case MfmaTile::Small: break;
     }
     return launch_tiles<SmallCfg, TA, TB>(p, stream);

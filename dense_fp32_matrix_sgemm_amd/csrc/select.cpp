@@ -12,8 +12,10 @@
 // unit hide more latency, so rate grows with q. The rates are measured on
 // MI355X with each shape forced over a set of products (TFLOP/s over 256
 // compute units, relative to 147 for 256x256 at 4096^3): 128x128 0.88 alone
-// and 0.93 two at a time; 64x64 0.59, 0.72, 0.79 and 0.84 for one to four.
-// (A 256x128 shape measured 0.85-0.94 alone and never beat these three.)
+// and 0.93 two at a time; 64x64 0.59, 0.72, 0.79 and 0.84 for one to four;
+// 64x64 with its K range split over two sets of waves 0.65 alone and 0.78 two
+// at a time (it takes 1024^3 from 80 to 95 TFLOP/s). (A 256x128 shape
+// measured 0.85-0.94 alone and never beat these.)
 //
 // Pure C++ (no HIP), so it is tested on the host.
 #include <cstddef>
@@ -48,6 +50,7 @@ const Candidate kCandidates[] = {
     {MfmaTile::Big, tiles::kBig[0], tiles::kBig[1], 1, {1.0, 0, 0, 0}},
     {MfmaTile::Mid, tiles::kMid[0], tiles::kMid[1], 2, {0.88, 0.93, 0, 0}},
     {MfmaTile::Small, tiles::kSmall[0], tiles::kSmall[1], 4, {0.59, 0.72, 0.79, 0.84}},
+    {MfmaTile::KSplit, tiles::kKSplit[0], tiles::kKSplit[1], 2, {0.65, 0.78, 0, 0}},
 };
 
 }  // namespace
@@ -57,7 +60,7 @@ MfmaTile choose_mfma_tile(int M, int N, int cus)
     const std::int64_t n_cus = cus > 0 ? cus : 256;
     MfmaTile best = MfmaTile::Big;
     double best_t = -1.0;
-    for (const Candidate &c : kCandidates) {  // ties go to the larger tile (less traffic)
+    for (const Candidate &c : kCandidates) {  // ties go to the earlier (larger or simpler) shape
         const double t = launch_time(c, M, N, n_cus);
         if (best_t < 0.0 || t < best_t) {
             best_t = t;
@@ -159,6 +162,7 @@ extern "C" int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN)
     case MfmaTile::Big: dims = tiles::kBig; break;
     case MfmaTile::Mid: dims = tiles::kMid; break;
     case MfmaTile::Small: dims = tiles::kSmall; break;
+    case MfmaTile::KSplit: dims = tiles::kKSplit; break;
     }
     *BM = dims[0];
     *BN = dims[1];
@@ -175,4 +179,25 @@ extern "C" std::size_t sgemm_ex_workspace_size(int transA, int transB, int M, in
     if ((transA == SGEMM_OP_T && M < 4) || (transB == SGEMM_OP_N && N < 4)) return 0;
     const SplitChoice c = choose_split(M, N, K, cus);
     return c.use ? c.bytes : 0;
+}
+
+extern "C" int sgemm_mfma_shape(int M, int N, int cus, int *shape)
+{
+    using namespace sgemm_impl;
+    if (M < 0 || N < 0) return SGEMM_ERR_DIM;
+    if (shape == nullptr) return SGEMM_ERR_NULL;
+    const int *dims = tiles::kSmall;
+    int sets = 1;
+    switch (choose_mfma_tile(M, N, cus)) {
+    case MfmaTile::Big: dims = tiles::kBig; break;
+    case MfmaTile::Mid: dims = tiles::kMid; break;
+    case MfmaTile::Small: dims = tiles::kSmall; break;
+    case MfmaTile::KSplit:
+        dims = tiles::kKSplit;
+        sets = tiles::kKSplit[5];
+        break;
+    }
+    for (int i = 0; i < 5; ++i) shape[i] = dims[i];
+    shape[5] = sets;
+    return SGEMM_OK;
 }

@@ -21,17 +21,24 @@
 #ifndef SGEMM_MFMA_SMALL_TILE
 #define SGEMM_MFMA_SMALL_TILE 64, 64, 32, 2, 2
 #endif
+// The small tile with its K range split over two sets of waves (BM, BN, BK,
+// WAVES_M, WAVES_N, sets): two waves per SIMD where one small tile per
+// compute unit would leave one.
+#ifndef SGEMM_MFMA_KSPLIT_TILE
+#define SGEMM_MFMA_KSPLIT_TILE 64, 64, 64, 2, 2, 2
+#endif
 
 namespace sgemm_impl {
 
 // Interior tile shape of one matrix-core launch.
-enum class MfmaTile { Big, Mid, Small };
+enum class MfmaTile { Big, Mid, Small, KSplit };
 
 namespace tiles {
 constexpr int kGeneral[] = {SGEMM_MFMA_TILE};
 constexpr int kBig[] = {SGEMM_MFMA_BIG_TILE};
 constexpr int kMid[] = {SGEMM_MFMA_MID_TILE};
 constexpr int kSmall[] = {SGEMM_MFMA_SMALL_TILE};
+constexpr int kKSplit[] = {SGEMM_MFMA_KSPLIT_TILE};
 }  // namespace tiles
 
 }  // namespace sgemm_impl

@@ -299,6 +299,16 @@ int sgemm_best_variant(int M, int N, int K);
  */
 int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN);
 
+/*
+ * The whole kernel shape behind sgemm_mfma_tile's choice, in shape[0..5]:
+ * BM, BN, BK (slab depth), the waves per work-group along M and N, and the
+ * number of wave sets that split each slab's k between them (1, or 2 for the
+ * 64 x 64 tile that puts two waves on each SIMD when one such tile per
+ * compute unit would leave one). Pure host logic. Returns SGEMM_OK,
+ * SGEMM_ERR_DIM or SGEMM_ERR_NULL (shape NULL).
+ */
+int sgemm_mfma_shape(int M, int N, int cus, int *shape);
+
 #ifdef __cplusplus
 }
 #endif

@@ -216,6 +216,21 @@ def test_mfma_tile_choice(lib):
     assert sg.sgemm_mfma_tile(4096, 4096, cus=0) == sg.sgemm_mfma_tile(4096, 4096, cus=256)
 
 
+def test_mfma_shape_choice(lib):
+    # One 64x64 tile per compute unit takes the two-set K-split tile (two
+    # waves per SIMD); several resident per compute unit, the plain one.
+    assert sg.sgemm_mfma_shape(1024, 1024) == (64, 64, 64, 2, 2, 2)
+    assert sg.sgemm_mfma_shape(1000, 1000) == (64, 64, 64, 2, 2, 2)
+    assert sg.sgemm_mfma_shape(3001, 2047) == (64, 64, 32, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(4096, 4096) == (256, 256, 16, 4, 2, 1)
+    assert sg.sgemm_mfma_shape(2048, 2048) == (128, 128, 32, 2, 4, 1)
+    for shape in [(7, 9), (128, 128), (1024, 1024), (3001, 2047), (4096, 4096), (8192, 300)]:
+        assert sg.sgemm_mfma_shape(*shape)[:2] == sg.sgemm_mfma_tile(*shape)
+    shp = (ctypes.c_int * 6)()
+    assert lib.sgemm_mfma_shape(-1, 4, 0, shp) == sg.SGEMM_ERR_DIM
+    assert lib.sgemm_mfma_shape(4, 4, 0, None) == sg.SGEMM_ERR_NULL
+
+
 def test_mfma_tile_errors(lib):
     bm, bn = ctypes.c_int(), ctypes.c_int()
     assert lib.sgemm_mfma_tile(-1, 4, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_ERR_DIM

@@ -4,9 +4,10 @@ Tiles that cross the bottom or right edge of C run the same loop as the
 others, with their reads clamped into the operands and the partial chunk of
 a row-contiguous operand read from a shifted address and rotated into place.
 These tests run ragged products whose chosen tile shape (each of 256x256,
-128x128 and 64x64) leaves partial tiles on both edges, for every transpose
-pair, with alpha and beta, and the narrowest widths the clamped reads allow
-(4 to 7) next to the general path below them. Every comparison is with the
+128x128, 64x64 and the 64x64 tile whose slabs two wave sets share) leaves
+partial tiles on both edges, for every transpose pair, with alpha and beta,
+and the narrowest widths the clamped reads allow (4 to 7) next to the general
+path below them. Every comparison is with the
 oracle; sampled outputs always include the last rows and columns.
 """
 
@@ -37,9 +38,12 @@ def _stored(x, trans):
     return np.ascontiguousarray(x.T) if trans else x
 
 
-# (M, N, K) and the tile shape the library picks for it (checked on the host).
+# (M, N, K) and the tile shape the library picks for it (checked on the host);
+# 1000^3 takes the two-set 64x64 tile (one tile per compute unit), with a
+# partial last slab (1000 = 15 * 64 + 40).
 RAGGED = [((5000, 3000, 333), (256, 256)), ((4300, 4300, 130), (128, 128)), ((3001, 2047, 4093), (64, 64)),
           ((1900, 2100, 77), (128, 128)), ((1000, 1000, 1000), (64, 64))]
+KSPLIT = {(1000, 1000, 1000)}
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
@@ -48,6 +52,7 @@ def test_edge_tiles_of_every_shape(shape, tile, pair):
     M, N, K = shape
     tA, tB = pair
     assert sg.sgemm_mfma_tile(M, N) == tile
+    assert (sg.sgemm_mfma_shape(M, N)[5] == 2) == (shape in KSPLIT)
     print(f"[edges] {M}x{N}x{K} tile {tile} pair {pair}", flush=True)
     opA = synth.uniform_pm1(M + 11, (M, K))
     opB = synth.uniform_pm1(N + 12, (K, N))
