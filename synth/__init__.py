@@ -153,3 +153,26 @@ def operands(M: int, N: int, K: int, dist: str = "u01",
     """Return (A, B) as contiguous float32 arrays of shape (M, K) and (K, N)."""
     gen = {"u01": uniform01, "pm1": uniform_pm1, "int": small_int}[dist]
     return gen(seed_a, (M, K)), gen(seed_b, (K, N))
+
+
+# Closed-form integer patterns for products too large to draw on the host: the
+# element (r, c) of a pattern (mul_r, mul_c, mod) is ((r * mul_r + c * mul_c)
+# mod mod) - mod // 2, a small integer (exact in float32, bf16 and f16 for
+# mod <= 33). ``pattern_rows`` gives chosen rows on the host; ``pattern_device``
+# fills a whole matrix on a GPU with torch, in row blocks.
+def pattern_rows(rows, cols: int, mul_r: int, mul_c: int, mod: int) -> np.ndarray:
+    r = np.asarray(rows, dtype=np.int64)[:, None]
+    c = np.arange(cols, dtype=np.int64)[None, :]
+    return (((r * mul_r + c * mul_c) % mod) - mod // 2).astype(np.float32)
+
+
+def pattern_device(rows: int, cols: int, mul_r: int, mul_c: int, mod: int, device, dtype=None, block: int = 4096):
+    """A rows x cols torch tensor of the pattern on `device` (float32, or
+    `dtype`), built a block of rows at a time to bound temporaries."""
+    import torch
+    out = torch.empty((rows, cols), dtype=dtype or torch.float32, device=device)
+    c = torch.arange(cols, dtype=torch.int64, device=device)[None, :] * mul_c
+    for r0 in range(0, rows, block):
+        r = torch.arange(r0, min(rows, r0 + block), dtype=torch.int64, device=device)[:, None] * mul_r
+        out[r0:r0 + r.shape[0]] = (((r + c) % mod) - mod // 2).to(out.dtype)
+    return out
