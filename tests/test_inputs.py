@@ -62,3 +62,19 @@ def test_embed_pads_with_fill():
     assert np.isnan(buf[:, 7:]).all()
     with pytest.raises(ValueError):
         synth.embed(x, 6)
+
+
+def test_integer_patterns_agree_on_host_and_device():
+    # The two builders of a closed-form pattern give the same matrix (torch on
+    # the CPU stands in for the device here), in block-sized pieces too, and
+    # the values are the small integers the formula names.
+    import torch
+    for (rows, cols, mr, mc, mod, block) in [(1000, 40, 7, 13, 17, 300), (37, 4100, 5, 3, 11, 8), (5, 5, 1, 1, 3, 2)]:
+        t = synth.pattern_device(rows, cols, mr, mc, mod, "cpu", block=block).numpy()
+        h = synth.pattern_rows(np.arange(rows), cols, mr, mc, mod)
+        assert np.array_equal(t, h)
+        r, c = 3, 4
+        assert h[r, c] == ((r * mr + c * mc) % mod) - mod // 2
+        assert h.min() >= -(mod // 2) and h.max() <= mod - 1 - mod // 2
+    b = synth.pattern_device(64, 64, 7, 13, 17, "cpu", dtype=torch.bfloat16)
+    assert torch.equal(b.float(), synth.pattern_device(64, 64, 7, 13, 17, "cpu"))
