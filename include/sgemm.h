@@ -22,9 +22,10 @@
  *
  * All matrix pointers are DEVICE pointers on the calling thread's current HIP
  * device. The caller owns every buffer; the library allocates nothing per
- * call, keeps no pointer after returning and has no mutable global state
- * besides a per-device cache of the device's architecture, so calls from
- * several host threads are safe.
+ * call (sgemm_ex_ws works in scratch memory the caller passes), keeps no
+ * pointer after returning and has no mutable global state besides a
+ * per-device cache of the device's architecture, so calls from several host
+ * threads are safe.
  */
 #ifndef SGEMM_H
 #define SGEMM_H
@@ -71,7 +72,8 @@ typedef enum sgemm_op {
  *           registers, 128-bit global loads, double-buffered LDS (same page,
  *           section 07; "From 306 ms to 86 ms", "Register blocking").
  *  MFMA     the same tiling fed to the CDNA matrix cores with
- *           v_mfma_f32_32x32x2_f32 (FP32 in, FP32 accumulate).
+ *           v_mfma_f32_32x32x2_f32 (FP32 in, FP32 accumulate), with the tile
+ *           shape chosen per product (sgemm_mfma_tile, sgemm_mfma_shape).
  *  BEST     whichever variant is fastest for the shape (currently MFMA). */
 typedef enum sgemm_variant {
     SGEMM_BEST = -1,
