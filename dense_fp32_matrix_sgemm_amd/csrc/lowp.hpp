@@ -416,7 +416,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void lp
 // loads have one slab of MFMAs to arrive. With 16-bit operands the matrix
 // cores finish a slab 8 times sooner, relative to the bytes it moves, than in
 // FP32, and that loop leaves them waiting on load latency and LDS bandwidth.
-// This one differs in three ways:
+// This one differs in four ways:
 //  * four waves (2 x 2) each multiply a 128 x 128 block of the 256 x 256
 //    tile (16 accumulator blocks, one wave per SIMD): per slab the waves read
 //    2/3 of the LDS bytes that eight 64 x 128 waves read;
@@ -432,7 +432,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void lp
 //    chunk j at position j ^ h(k), h(k) = ((k & 3) << 2) ^ (k & 2). With
 //    these the lanes of a ds_read_b128 or ds_read_b64_tr_b16 that the LDS
 //    serves together fall in distinct banks, for 32 four-byte banks serving
-//    128 bytes per cycle and for 64 serving 256.
+//    128 bytes per cycle and for 64 serving 256;
+//  * the accumulators leave through LDS (the stages are free by then), so
+//    that every store writes 512 contiguous bytes of each of two rows of C.
 // A barrier per slab publishes the next stage (each wave first waits for its
 // own DMA of it, with the s_waitcnt count of the loads it may leave in
 // flight) and frees the stage the DMA issued after it overwrites. The
@@ -613,24 +615,29 @@ __device__ __forceinline__ void lp_dma_tile(const LpProblem &p, int tm, int tn, 
         else
             read_op(OpB{}, fb[slot][u - NA], stage_b(st), offb[s][u - NA]);
     };
+    // The instruction takes B's fragment as its first operand and A's as its
+    // second, and so computes the transpose of block (a, b): lane l holds
+    // row l % 32 of the block and, in registers 4q .. 4q + 3, its columns
+    // 8q + 4h .. 8q + 4h + 3. The fragments are the same either way (both
+    // operands take 8 k of one free index per lane), and so are the sums.
     auto mfma_one = [&](int slot, int i) {
         const int a = i / NBl, b = i % NBl;
-        acc[a][b] = mma16<T>(fa[slot][a], fb[slot][b], acc[a][b]);
+        acc[a][b] = mma16<T>(fb[slot][b], fa[slot][a], acc[a][b]);
     };
 
     // One step's MFMAs with the fragment reads for the other slot spread one
     // after each of the first MFMAs (so reads neither hold back an MFMA nor
-    // wait until the MFMAs that need them), and, after the barrier, the
-    // slab's DMA instructions spread the same way (each is its own
+    // wait until the MFMAs that need them), and DMA instructions d0 .. d0 +
+    // nd - 1 of a slab spread evenly over the step (each is its own
     // scheduling region, which keeps the order as written).
     constexpr int kReads = (OpA::KC ? NA : 2 * NA) + (OpB::KC ? NBl : 2 * NBl);
     constexpr int kMfmas = NA * NBl;
     static_assert(kReads <= kMfmas && NU <= kMfmas && kPerSlab <= kMfmas, "one read and one DMA per MFMA at most");
-    auto step = [&](int slot, int rd_st, int rd_s, bool reads, int dma_slab, bool dmas) {
-        const int dma_st = (rd_st + S - 2) % S;  // with dmas: the stage of slab t - 1
+    auto step = [&](int slot, int rd_st, int rd_s, bool reads, int dma_slab, int dma_st, int d0, int nd) {
 #pragma unroll
         for (int i = 0; i < kMfmas; ++i) {
-            if (dmas && i < kPerSlab) dma_one(i, dma_slab, dma_st);
+            if (nd > 0 && i % (kMfmas / nd) == 0 && i / (kMfmas / nd) < nd)
+                dma_one(d0 + i / (kMfmas / nd), dma_slab, dma_st);
             mfma_one(slot, i);
             if (reads && i < NU) read_unit(i, rd_st, rd_s, slot ^ 1);
         }
@@ -655,15 +662,25 @@ __device__ __forceinline__ void lp_dma_tile(const LpProblem &p, int tm, int tn, 
         lp_wait_barrier<(S - 2) * kPerSlab>();
 #pragma unroll
         for (int u = 0; u < NU; ++u) read_unit(u, 0, 0, 0);
-        // Step 0 of slab t multiplies while step 1's fragments load; slab
-        // t + 1 is published (slabs t + 2 .. t + S - 2 may still be in
-        // flight); step 1 multiplies while slab t + S - 1 is requested into
-        // the stage slab t - 1 used and slab t + 1's first fragments load (in
-        // the last iteration, from a stage nobody uses again).
+        // Slab t + S - 1 goes into the stage slab t - 1 used, which the
+        // barrier before step 0 of slab t frees: its first kEarly DMA
+        // instructions go out during step 0, the rest during step 1, so the
+        // two steps carry equal LDS traffic. Step 0 of slab t multiplies
+        // while step 1's fragments load; slab t + 1 is published (slabs
+        // t + 2 .. t + S - 2 and the early part of t + S - 1 may still be in
+        // flight); step 1 multiplies while slab t + 1's first fragments load
+        // (in the last iteration, from a stage nobody uses again).
+#if defined(SGEMM_LP_DMA_EARLY)
+        constexpr int kEarly = SGEMM_LP_DMA_EARLY;
+#else
+        constexpr int kEarly = kPerSlab / 2;
+#endif
+        static_assert(kEarly >= 0 && kEarly <= kPerSlab, "a split of the slab's DMA instructions");
         for (int t = 0; t < n; ++t) {
-            step(0, t % S, 1, true, 0, false);
-            lp_wait_barrier<(S - 3) * kPerSlab>();
-            step(1, (t + 1) % S, 0, true, last(t + S - 1), true);
+            const int dma_st = (t + S - 1) % S, dma_slab = last(t + S - 1);
+            step(0, t % S, 1, true, dma_slab, dma_st, 0, kEarly);
+            lp_wait_barrier<(S - 3) * kPerSlab + kEarly>();
+            step(1, (t + 1) % S, 0, true, dma_slab, dma_st, kEarly, kPerSlab - kEarly);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated DMAs
     }
@@ -690,24 +707,44 @@ __device__ __forceinline__ void lp_dma_tile(const LpProblem &p, int tm, int tn, 
         lp_wait_barrier<0>();
 #pragma unroll
         for (int u = 0; u < NU; ++u) read_unit(u, 0, 0, 0);
-        step(0, 0, 1, true, 0, false);
-        step(1, 0, 0, false, 0, false);
+        step(0, 0, 1, true, 0, 0, 0, 0);
+        step(1, 0, 0, false, 0, 0, 0, 0);
     }
 
-    // Epilogue: register r of block (a, b) is row 32a + 8(r/4) + 4h + r%4 and
-    // column 32b + l % 32 of the wave tile.
+    // Epilogue through LDS, one block row (32 rows of the wave tile) at a
+    // time: each lane writes its 4-column pieces (register r of block (a, b)
+    // is row 32a + l % 32, column 32b + 8(r/4) + 4h + r%4), then reads back 4
+    // consecutive columns of a row, so that one store covers two rows of 512
+    // contiguous bytes. (Stored straight from the accumulators, one store
+    // covers 32 bytes of each of 32 rows, which is slow when the rows are a
+    // large power of two apart.) Rows are padded by 4 floats, which puts the
+    // 16 lanes an LDS pass serves in distinct banks for the writes and the
+    // reads. Every wave stages in its own 32-row region; the barrier first
+    // makes sure that no DMA or fragment read still uses the stages.
     const bool inside = m0 + BM <= p.M && n0 + BN <= p.N;
+    constexpr int kPitch = Cfg::WN + 4;
+    static_assert(NW * 32 * kPitch * 2 <= S * kStage, "staging fits in the operand stages");
+    lp_wait_barrier<0>();
+    float *stage_c = reinterpret_cast<float *>(lds) + wave * 32 * kPitch;
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+    for (int a = 0; a < NA; ++a) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const std::int64_t row = m0 + wm0 + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
+        for (int b = 0; b < NBl; ++b)
 #pragma unroll
-            for (int b = 0; b < NBl; ++b) {
-                const float v[1] = {acc[a][b][r]};
-                update_n<1>(p.C, p.ldc, row, n0 + wn0 + 32 * b + l32, p.M, p.N, v, inside, p.alpha, p.beta);
-            }
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4u *>(stage_c + l32 * kPitch + 32 * b + 8 * q + 4 * h) =
+                    f32x4u{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's writes before its reads
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int row = 2 * it + h;
+            const f32x4u x = *reinterpret_cast<const f32x4u *>(stage_c + row * kPitch + 4 * l32);
+            const float v[4] = {x[0], x[1], x[2], x[3]};
+            update_n<4>(p.C, p.ldc, m0 + wm0 + 32 * a + row, n0 + wn0 + 4 * l32, p.M, p.N, v, inside, p.alpha,
+                        p.beta);
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads before the next block row's writes
+    }
 }
 
 template <class Cfg, LpType T, bool TA, bool TB>
