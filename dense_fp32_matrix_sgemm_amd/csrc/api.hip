@@ -3,6 +3,7 @@
 
 #include <atomic>
 #include <cstddef>
+#include <cstdint>
 #include <cstring>
 
 #include "gemm.hpp"
@@ -60,7 +61,11 @@ extern "C" int sgemm_ex_ws(int transA, int transB, int M, int N, int K, float al
     if (rc != SGEMM_OK) return rc;
     const bool product = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
     const int v = variant == SGEMM_BEST ? sgemm_best_variant(M, N, K) : variant;
-    if (product && v == SGEMM_MFMA && workspace != nullptr && workspace_bytes > 0) {
+    // The adding kernel reads the partial tiles with 16-byte loads, so a
+    // workspace that is not 16-byte aligned is not used.
+    const bool ws_usable =
+        workspace != nullptr && workspace_bytes > 0 && reinterpret_cast<std::uintptr_t>(workspace) % 16 == 0;
+    if (product && v == SGEMM_MFMA && ws_usable) {
         const int cus = current_gfx950_cus();
         if (cus == 0) return SGEMM_ERR_DEVICE;
         const std::size_t need = sgemm_ex_workspace_size(transA, transB, M, N, K, cus);

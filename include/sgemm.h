@@ -201,8 +201,9 @@ int sgemm_ex_check_args(int transA, int transB, int M, int N, int K,
  * (its last bits may differ from sgemm_ex's, whose sums are not split).
  *
  * Arguments: those of sgemm_ex, plus
- *   workspace        device memory the call may use (contents undefined
- *                    afterwards; the caller owns it); NULL, or
+ *   workspace        16-byte aligned device memory the call may use
+ *                    (contents undefined afterwards; the caller owns it);
+ *                    NULL, an address that is not 16-byte aligned, or
  *   workspace_bytes  smaller than sgemm_ex_workspace_size() for this product,
  *                    makes the call exactly sgemm_ex.
  * The library decides per product whether the split schedule is faster; only

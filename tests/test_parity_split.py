@@ -8,7 +8,7 @@ second kernel. These tests run products the library puts on that schedule
 pair, alpha and beta, ragged edges and a partial last K slab, against the
 oracle; and check that results repeat bit for bit, that the workspace's prior
 contents do not matter, that nothing outside C's window is written, and that
-a missing or short workspace gives exactly sgemm_ex.
+a missing, short or misaligned workspace gives exactly sgemm_ex.
 """
 
 import numpy as np
@@ -128,8 +128,12 @@ def test_short_or_missing_workspace_is_exactly_sgemm_ex(workspace):
     plain = gemm_ex(False, True, 2.0, A, B, 0.5, C0, "mfma")
     short = gemm_ex(False, True, 2.0, A, B, 0.5, C0, "mfma", workspace=workspace[: need - 1])
     empty = gemm_ex(False, True, 2.0, A, B, 0.5, C0, "mfma", workspace=workspace[:0])
+    # Large enough but not 16-byte aligned (the fixture's storage is).
+    assert workspace.data_ptr() % 16 == 0
+    skewed = gemm_ex(False, True, 2.0, A, B, 0.5, C0, "mfma", workspace=workspace[4:4 + need])
     assert np.array_equal(plain.view(np.uint32), short.view(np.uint32))
     assert np.array_equal(plain.view(np.uint32), empty.view(np.uint32))
+    assert np.array_equal(plain.view(np.uint32), skewed.view(np.uint32))
     # Other variants ignore the workspace.
     tiled = gemm_ex(False, True, 2.0, A, B, 0.5, C0, "tiled")
     tiled_ws = gemm_ex(False, True, 2.0, A, B, 0.5, C0, "tiled", workspace=workspace)
