@@ -231,6 +231,17 @@ def _storage(t, name):
     raise ValueError(f"{name} must be row-major or column-major (strides {(s0, s1)})")
 
 
+_INT32_MAX = 2**31 - 1
+
+
+def _check_int32(**sizes):
+    """The C ABI takes sizes and leading dimensions as C int; ctypes would
+    wrap a larger value silently (2**32 + 8 arrives as 8), so refuse it."""
+    for name, v in sizes.items():
+        if not 0 <= v <= _INT32_MAX:
+            raise ValueError(f"{name} = {v} is outside the C ABI's int range [0, {_INT32_MAX}]")
+
+
 def _check_tensor(t, name):
     import torch
 
@@ -280,6 +291,7 @@ def gemm(A, B, C=None, alpha=1.0, beta=0.0, variant="best", workspace=None):
     tc, ldc = _storage(C, "C")
     if tc != SGEMM_OP_N:
         raise ValueError("C must be row-major (unit column stride)")
+    _check_int32(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     with torch.cuda.device(A.device):
         stream = torch.cuda.current_stream(A.device).cuda_stream
         if workspace is None:
@@ -328,6 +340,7 @@ def _gemm_lp(A, B, C, alpha, beta, dtype):
     tc, ldc = _storage(C, "C")
     if tc != SGEMM_OP_N:
         raise ValueError("C must be row-major (unit column stride)")
+    _check_int32(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     with torch.cuda.device(A.device):
         stream = torch.cuda.current_stream(A.device).cuda_stream
         rc = sgemm_lp(dtype, ta, tb, M, N, K, float(alpha), A.data_ptr() or None, lda,

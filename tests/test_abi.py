@@ -186,6 +186,18 @@ def test_storage_order_of_tensor_views():
         sg._storage(x[::2, ::2], "x")
 
 
+def test_sizes_beyond_int_are_refused_not_wrapped():
+    # ctypes passes 2**32 + 8 to a C int as 8; the binding refuses such sizes.
+    sg._check_int32(M=0, N=1, K=2**31 - 1, lda=7)
+    for bad in (2**31, 2**32 + 8, -1):
+        with pytest.raises(ValueError, match="int range"):
+            sg._check_int32(M=4, N=4, K=4, lda=bad)
+    # A stride past int range (a meta tensor: shape and strides, no storage).
+    import torch
+    x = torch.empty_strided((2, 3), (2**32 + 8, 1), device="meta")
+    assert sg._storage(x, "x") == (N_, 2**32 + 8)
+
+
 def test_matmul_rejects_bad_tensors():
     import torch
     a = torch.zeros(3, 4)
