@@ -184,6 +184,29 @@ def test_lp_direct_to_lds_small_integers_bit_exact(pair):
     assert np.array_equal(C.astype(np.float64), want)
 
 
+@pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
+def test_lp_direct_to_lds_padded_c(pair):
+    # The direct-to-LDS kernel's epilogue (C staged through LDS, stored four
+    # columns at a time) into a C whose rows are padded to an odd length and
+    # whose start is 12 bytes past a 16-byte boundary; A and B keep what that
+    # kernel needs (16-byte aligned, leading dimensions padded by 8), and the
+    # product is ragged on both edges. Equal bit for bit to the packed run,
+    # and nothing outside C's window changes.
+    tA, tB = pair
+    M, N, K = 4000, 4104, 520
+    print(f"[lowp] direct-to-LDS padded C {pair}", flush=True)
+    opA, opB, C0 = _case("bf16", M, N, K, 95)
+    A = synth.to_lowp_bits(_stored(opA, tA), "bf16")
+    B = synth.to_lowp_bits(_stored(opB, tB), "bf16")
+    packed = gemm_lp("bf16", tA, tB, 1.5, A, B, -0.25, C0)
+    C, cbuf, ldc, off = gemm_lp("bf16", tA, tB, 1.5, A, B, -0.25, C0, ld_pad=(8, 8, 9), offset=(0, 0, 3),
+                                return_buffer=True)
+    assert np.array_equal(C.view(np.uint32), packed.view(np.uint32)), pair
+    mask = np.ones(cbuf.shape, bool)
+    mask[(off + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]).ravel()] = False
+    assert (cbuf[mask] == SENTINEL).all()
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_lp_narrow_operands(dtype):
     # Row-contiguous free extents 1..12: under 8 the one-per-element kernel,
