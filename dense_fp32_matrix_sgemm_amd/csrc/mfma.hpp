@@ -83,11 +83,16 @@ __device__ __forceinline__ float elem(V v, int t)
     return v[t];
 }
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int REG_SETS_ = 1>
 struct MfmaConfig {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+    // Register sets that stage slabs on their way global -> LDS: with one,
+    // a slab's loads are issued one slab before it is stored to LDS; with two,
+    // two slabs before.
+    static constexpr int kRegSets = REG_SETS_;
+    static_assert(kRegSets == 1 || kRegSets == 2, "one or two staging register sets");
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
 #ifndef SGEMM_MFMA_GROUP_M
 #define SGEMM_MFMA_GROUP_M 8
@@ -520,23 +525,26 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
     const OperandSource<OpB, EDGE> srcb(p.B, p.ldb, n0, p.N, tid);
     const std::int64_t slab_a = OpA::KC ? BK : BK * p.lda, slab_b = OpB::KC ? BK : BK * p.ldb;
 
-    f32x4 ra[CA], rb[CB];
-    auto fetch = [&](int slab) {  // slab counted from s_first
+    // Slab s is staged in register set s % RS; `set` is always a constant
+    // after unrolling, so the sets stay in fixed registers.
+    constexpr int RS = Cfg::kRegSets;
+    f32x4 ra[RS][CA], rb[RS][CB];
+    auto fetch = [&](int slab, int set) {  // slab counted from s_first
         const std::int64_t ka = (s_first + slab) * slab_a, kb = (s_first + slab) * slab_b;
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            ra[q] = load16u(srca.chunk(q) + ka);
+            ra[set][q] = load16u(srca.chunk(q) + ka);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            rb[q] = load16u(srcb.chunk(q) + kb);
+            rb[set][q] = load16u(srcb.chunk(q) + kb);
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, int set) {
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[q]);
+            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[set][q]);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[q]);
+            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[set][q]);
     };
 
     typename OpA::Frag fa[2];
@@ -586,39 +594,75 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
 
     const int n = s_stop - s_first;
     if (n > 0) {
-        fetch(0);
-        stash(0);
-        if (n > 1) fetch(1);
+        fetch(0, 0);
+        stash(0, 0);
+        if (n > 1) fetch(1, RS - 1);
+        if (RS == 2 && n > 2) fetch(2, 0);
         __syncthreads();
         read_frags(0, 0, 0);
         int t = 0;
         // Steady state, one straight-line block per slab t (LDS buffer cur):
         //   A: store slab t+1 (registers) to buffer cur^1, start loading slab
-        //      t+2, read groups 1..G-1 of slab t while multiplying groups
-        //      0..G-2;
+        //      t+1+RS into the registers just freed, read groups 1..G-1 of
+        //      slab t while multiplying groups 0..G-2;
         //   barrier: slab t+1 is complete in LDS, and every wave has finished
         //      reading buffer cur^1's previous contents (slab t-1, before the
         //      previous barrier);
         //   B: read group 0 of slab t+1 while multiplying group G-1 of slab t.
-        for (; t + 2 < n; ++t) {
-            const int cur = t & 1;
-            stash(cur ^ 1);
-            fetch(t + 2);
+        if constexpr (RS == 1) {
+            for (; t + 2 < n; ++t) {
+                const int cur = t & 1;
+                stash(cur ^ 1, 0);
+                fetch(t + 2, 0);
 #pragma unroll
-            for (int g = 0; g + 1 < G; ++g) {
-                read_frags(cur, g + 1, (g + 1) & 1);
-                mfmas(g & 1);
+                for (int g = 0; g + 1 < G; ++g) {
+                    read_frags(cur, g + 1, (g + 1) & 1);
+                    mfmas(g & 1);
+                }
+                interleave_a();
+                __syncthreads();
+                read_frags(cur ^ 1, 0, 0);
+                mfmas((G - 1) & 1);
+                interleave_b();
             }
-            interleave_a();
-            __syncthreads();
-            read_frags(cur ^ 1, 0, 0);
-            mfmas((G - 1) & 1);
-            interleave_b();
+        } else {
+            // Two slabs per iteration, so that each names its register set
+            // as a constant (slab t+1 is in set (t+1) & 1, and t is even).
+            static_assert(CA + CB < 16, "the wait count below fits its field");
+            auto steady = [&](int t, auto set) {
+                const int cur = t & 1;
+                // Loads complete in order, so at most CA + CB outstanding
+                // (the other set's) means this set's have landed. The
+                // compiler's own count would also wait for the other set.
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (CA + CB));  // vmcnt(CA+CB), expcnt/lgkmcnt: no wait
+                stash(cur ^ 1, decltype(set)::value);
+                fetch(t + 3, decltype(set)::value);
+#pragma unroll
+                for (int g = 0; g + 1 < G; ++g) {
+                    read_frags(cur, g + 1, (g + 1) & 1);
+                    mfmas(g & 1);
+                }
+                interleave_a();
+                __syncthreads();
+                read_frags(cur ^ 1, 0, 0);
+                mfmas((G - 1) & 1);
+                interleave_b();
+            };
+            for (; t + 4 < n; t += 2) {
+                steady(t, std::integral_constant<int, 1>{});
+                steady(t + 1, std::integral_constant<int, 0>{});
+            }
+            if (t + 3 < n) steady(t++, std::integral_constant<int, 1>{});
         }
-        // Last two slabs: no more loads.
+        // Last slabs: no more loads.
         for (; t < n; ++t) {
             const int cur = t & 1;
-            if (t + 1 < n) stash(cur ^ 1);
+            if (t + 1 < n) {
+                if (RS == 2 && ((t + 1) & 1) == 1)
+                    stash(cur ^ 1, RS - 1);
+                else
+                    stash(cur ^ 1, 0);
+            }
 #pragma unroll
             for (int g = 0; g + 1 < G; ++g) {
                 read_frags(cur, g + 1, (g + 1) & 1);
@@ -818,7 +862,7 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
 // Tile shapes (tiles.hpp).
 using GeneralCfg = MfmaConfig<SGEMM_MFMA_TILE>;
 using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
-using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
+using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE, SGEMM_MFMA_MID_REG_SETS>;
 using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
 using KSplitCfg = KSplitConfig<SGEMM_MFMA_KSPLIT_TILE>;
 

@@ -18,6 +18,13 @@
 #ifndef SGEMM_MFMA_MID_TILE
 #define SGEMM_MFMA_MID_TILE 128, 128, 32, 2, 4
 #endif
+// The 128x128 tile stages two slabs in registers (loads issued two slabs
+// before they are stored to LDS; +3-5% at 2048^3). The 256x256 tile has no
+// room for a second set, and the 64x64 tile, four work-groups per compute
+// unit, loses with one.
+#ifndef SGEMM_MFMA_MID_REG_SETS
+#define SGEMM_MFMA_MID_REG_SETS 2
+#endif
 #ifndef SGEMM_MFMA_SMALL_TILE
 #define SGEMM_MFMA_SMALL_TILE 64, 64, 32, 2, 2
 #endif
