@@ -101,7 +101,9 @@ struct MfmaConfig {
     // Waves per SIMD the register allocation aims at: one when a wave's
     // accumulators alone fill the 256 AGPRs, more as they shrink.
     static constexpr int kAccRegs = (WM / 32) * (WN / 32) * 16;
-    static constexpr int kWavesPerEU = kAccRegs >= 256 ? 1 : kAccRegs >= 64 ? 2 : 4;
+    // A second staging set needs more than the 128 registers of four waves
+    // per SIMD, so such a tile runs two (one eight-wave work-group per CU).
+    static constexpr int kWavesPerEU = kAccRegs >= 256 ? 1 : (kAccRegs >= 64 || REG_SETS_ == 2) ? 2 : 4;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK % 8 == 0, "slab depth must be whole groups of 8");
 };
@@ -863,6 +865,9 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
 using GeneralCfg = MfmaConfig<SGEMM_MFMA_TILE>;
 using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
 using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE, SGEMM_MFMA_MID_REG_SETS>;
+// The split schedule runs two 128x128 work-groups per compute unit at once,
+// which needs the one-set register budget.
+using MidSplitCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
 using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
 using KSplitCfg = KSplitConfig<SGEMM_MFMA_KSPLIT_TILE>;
 
@@ -1047,7 +1052,7 @@ hipError_t launch_sk(const Problem &p, float *ws, int grid, hipStream_t stream)
 template <bool TA, bool TB>
 hipError_t launch_sk_by_tile(const Problem &p, MfmaTile tile, float *ws, int grid, hipStream_t stream)
 {
-    if (tile == MfmaTile::Mid) return launch_sk<MidCfg, TA, TB>(p, ws, grid, stream);
+    if (tile == MfmaTile::Mid) return launch_sk<MidSplitCfg, TA, TB>(p, ws, grid, stream);
     return launch_sk<BigCfg, TA, TB>(p, ws, grid, stream);
 }
 

@@ -11,8 +11,9 @@
 // tile per compute unit runs at rate 1; more concurrent tiles per compute
 // unit hide more latency, so rate grows with q. The rates are measured on
 // MI355X with each shape forced over a set of products (TFLOP/s over 256
-// compute units, relative to 147 for 256x256 at 4096^3): 128x128 0.88 alone
-// and 0.93 two at a time; 64x64 0.59, 0.72, 0.79 and 0.84 for one to four;
+// compute units, relative to 147 for 256x256 at 4096^3): 128x128 0.91, one
+// at a time (its two staging register sets leave room for one work-group);
+// 64x64 0.59, 0.72, 0.79 and 0.84 for one to four;
 // 64x64 with its K range split over two sets of waves 0.65 alone and 0.78 two
 // at a time (it takes 1024^3 from 80 to 95 TFLOP/s). (A 256x128 shape
 // measured 0.85-0.94 alone and never beat these.)
@@ -48,7 +49,7 @@ double launch_time(const Candidate &c, std::int64_t M, std::int64_t N, std::int6
 
 const Candidate kCandidates[] = {
     {MfmaTile::Big, tiles::kBig[0], tiles::kBig[1], 1, {1.0, 0, 0, 0}},
-    {MfmaTile::Mid, tiles::kMid[0], tiles::kMid[1], 2, {0.88, 0.93, 0, 0}},
+    {MfmaTile::Mid, tiles::kMid[0], tiles::kMid[1], 1, {0.91, 0, 0, 0}},
     {MfmaTile::Small, tiles::kSmall[0], tiles::kSmall[1], 4, {0.59, 0.72, 0.79, 0.84}},
     {MfmaTile::KSplit, tiles::kKSplit[0], tiles::kKSplit[1], 2, {0.65, 0.78, 0, 0}},
 };

@@ -18,10 +18,12 @@
 #ifndef SGEMM_MFMA_MID_TILE
 #define SGEMM_MFMA_MID_TILE 128, 128, 32, 2, 4
 #endif
-// The 128x128 tile stages two slabs in registers (loads issued two slabs
-// before they are stored to LDS; +3-5% at 2048^3). The 256x256 tile has no
-// room for a second set, and the 64x64 tile, four work-groups per compute
-// unit, loses with one.
+// The 128x128 tile of whole-tile launches stages two slabs in registers
+// (loads issued two slabs before they are stored to LDS; +3-5% at 2048^3),
+// which takes the register budget of one work-group per compute unit. The
+// split schedule's 128x128 pieces keep one set (two work-groups per compute
+// unit), the 256x256 tile has no room for a second set, and the 64x64 tile
+// (four work-groups per compute unit) loses with one.
 #ifndef SGEMM_MFMA_MID_REG_SETS
 #define SGEMM_MFMA_MID_REG_SETS 2
 #endif
