@@ -24,6 +24,9 @@ Also reported:
   check         sampled elements compared with the oracle, and the
                 whole-matrix sum of C in double.
 
+With --cold it instead times the product with the caches flushed by a 512 MiB
+write before every launch, next to the same launches back to back.
+
 With --all-configs it instead times every kernel variant on every workload of
 the method's configuration table (128^3, 1024^3, 2048^3, 4096^3 and the ragged
 3001 x 2047 x 4093 on U[-1, 1)): median and minimum launch time, each result
@@ -112,6 +115,40 @@ def time_launches(call, steps: int, warmup: int):
     torch.cuda.synchronize()
     per = [events[i].elapsed_time(events[i + 1]) for i in range(steps)]
     return events[0].elapsed_time(events[steps]), per
+
+
+FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache; each XCD's 4 MB L2 goes with it
+
+
+def cold_cache(call, M: int, N: int, K: int, args, dev):
+    """The product with cold caches: before every timed launch a 512 MiB
+    buffer is written on the same stream, which evicts A, B and C from the L2
+    and the Infinity Cache, and HIP events bracket the product alone. The same
+    launches back to back (hot) are timed beside it."""
+    import torch
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        call()
+    cold = []
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    _, hot = time_launches(call, args.steps, 1)
+    f = flops(M, N, K)
+    res = {"config": {"M": M, "N": N, "K": K}, "flush_bytes": FLUSH_BYTES, "steps": args.steps}
+    for name, v in (("cold", cold), ("hot", hot)):
+        mean = sum(v) / len(v)
+        res[name] = {"kernel_ms_mean": round(mean, 5), "kernel_ms_min": round(min(v), 5),
+                     "TFLOP/s": round(f / (mean / 1e3) / 1e12, 3),
+                     "frac": round(f / (mean / 1e3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+    log(f"cold {res['cold']['kernel_ms_mean']:.4f} ms, hot {res['hot']['kernel_ms_mean']:.4f} ms")
+    return res
 
 
 def cpu_baseline(A, B, target_s: float):
@@ -277,6 +314,9 @@ def main(argv=None) -> int:
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the headline, time every variant on every configuration "
                          "and the CPU oracle on each")
+    ap.add_argument("--cold", action="store_true",
+                    help="instead of the headline line, time the product with the caches flushed "
+                         "(a 512 MiB write) before every launch, next to the same launches back to back")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the product, time a plain 256 MiB device copy "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -338,6 +378,11 @@ def main(argv=None) -> int:
             if rc != 0:
                 raise sg.SgemmError(rc)
         return call
+
+    if args.cold:
+        print(json.dumps({"metric": METRIC, "cold_cache": cold_cache(make_call(variant), M, N, K, args, dev)}),
+              flush=True)
+        return 0
 
     log(f"timing {args.steps} steps of variant {sg.sgemm_variant_name(resolved)} "
         f"after {args.warmup} warm-up steps")
