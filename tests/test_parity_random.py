@@ -8,7 +8,8 @@ list names are covered too. Sizes are log-uniform in [1, 3000] (FP32) or
 2048. Every case checks 600
 random entries plus the whole last row and column against the oracle, through
 sgemm_ex (variant best; every third case through sgemm_ex_ws with a workspace)
-for FP32 and through sgemm_lp for bf16 and f16.
+for FP32 and through sgemm_lp for bf16 and f16; a third set runs the naive,
+tiled and register-blocked rungs in turn.
 """
 
 import numpy as np
@@ -107,3 +108,23 @@ def test_random_lowp(case):
     want, S = oracle.gemm_ex_entries(tA, tB, alpha, oracle.lowp_to_float32(A, dtype), oracle.lowp_to_float32(B, dtype),
                                      beta, C0, rows, cols)
     assert_within(C[rows, cols], want, S, f"{dtype} {_id(case)}")
+
+
+RUNG_CASES = _cases(6072, 48, 1500)
+
+
+@pytest.mark.parametrize("case", RUNG_CASES, ids=_id)
+def test_random_every_rung(case):
+    # The same draws for the naive, tiled and register-blocked rungs, one per
+    # case in turn (the matrix-core rung is the "best" above).
+    i, M, N, K, tA, tB, alpha, beta, pads, offs = case
+    variant = ("naive", "tiled", "regblock")[i % 3]
+    print(f"[random] {variant} {_id(case)} alpha {alpha} beta {beta} pads {pads} offsets {offs}", flush=True)
+    opA = synth.uniform_pm1(3 * i + 201, (M, K))
+    opB = synth.uniform_pm1(3 * i + 202, (K, N))
+    C0 = synth.uniform_pm1(3 * i + 203, (M, N))
+    A, B = _stored(opA, tA), _stored(opB, tB)
+    C = gemm_ex(tA, tB, alpha, A, B, beta, C0, variant, ld_pad=pads, offset=offs)
+    rows, cols = _sample(M, N, i)
+    want, S = oracle.gemm_ex_entries(tA, tB, alpha, A, B, beta, C0, rows, cols)
+    assert_within(C[rows, cols], want, S, f"{variant} {_id(case)}")
