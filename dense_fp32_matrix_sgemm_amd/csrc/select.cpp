@@ -125,6 +125,8 @@ SplitChoice choose_split(int M, int N, int K, int cus)
     SplitChoice none{false, MfmaTile::Big, 0, 0};
     if (M <= 0 || N <= 0 || K <= 0) return none;
     const int n_cus = cus > 0 ? cus : 256;
+    constexpr int kMaxCus = 1 << 16;  // no device has more; keeps the grid (CUs x slots) in range
+    if (n_cus > kMaxCus) return none;
     // Whole tiles: the chosen shape's estimated time.
     const MfmaTile dp_tile = choose_mfma_tile(M, N, n_cus);
     const Candidate *dp = &kCandidates[0];
