@@ -162,3 +162,43 @@ def test_split_schedule_under_graph_capture():
         check(data, f"replay {rep}")
         torch.matmul(dA, dB).sum().item()   # eager work between replays
     del graph
+
+
+def test_host_threads_each_with_a_stream():
+    # The library keeps no per-call state and only a per-device cache of the
+    # architecture (an atomic per device), so host threads may call it at
+    # once, each on its own stream.
+    import threading
+    print("[graphs] four host threads", flush=True)
+    dev = torch.device("cuda:0")
+    shapes = [(700, 900, 500), (1024, 1024, 1024), (333, 2049, 777), (1500, 600, 1100)]
+    data = []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = synth.operands(M, N, K, "pm1", seed_a=70 + i, seed_b=80 + i)
+        data.append((A, B, torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
+                     [torch.empty((M, N), device=dev) for _ in range(3)]))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            _, _, dA, dB, outs = data[i]
+            with torch.cuda.stream(s):
+                for rep in range(12):
+                    sg.matmul(dA, dB, out=outs[rep % 3])
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for A, B, _, _, outs in data:
+        Cref, S = oracle.gemm(A, B, with_abs=True)
+        for dC in outs:
+            assert_within(dC.cpu().numpy(), Cref, S, "host threads")
