@@ -231,9 +231,9 @@ def test_mfma_tile_choice(lib):
 def test_mfma_shape_choice(lib):
     # One 64x64 tile per compute unit takes the two-set K-split tile (two
     # waves per SIMD); several resident per compute unit, the plain one.
-    assert sg.sgemm_mfma_shape(1024, 1024) == (64, 64, 64, 2, 2, 2)
-    assert sg.sgemm_mfma_shape(1000, 1000) == (64, 64, 64, 2, 2, 2)
-    assert sg.sgemm_mfma_shape(3001, 2047) == (64, 64, 32, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(1024, 1024) == (64, 64, 32, 2, 2, 2)
+    assert sg.sgemm_mfma_shape(1000, 1000) == (64, 64, 32, 2, 2, 2)
+    assert sg.sgemm_mfma_shape(3001, 2047) == (64, 64, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(4096, 4096) == (256, 256, 16, 4, 2, 1)
     assert sg.sgemm_mfma_shape(2048, 2048) == (128, 128, 32, 2, 4, 1)
     for shape in [(7, 9), (128, 128), (1024, 1024), (3001, 2047), (4096, 4096), (8192, 300)]:
