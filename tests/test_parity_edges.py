@@ -40,7 +40,7 @@ def _stored(x, trans):
 
 # (M, N, K) and the tile shape the library picks for it (checked on the host);
 # 1000^3 takes the two-set 64x64 tile (one tile per compute unit), with a
-# partial last slab (1000 = 15 * 64 + 40).
+# partial last slab (1000 = 31 * 32 + 8).
 RAGGED = [((5000, 3000, 333), (256, 256)), ((4300, 4300, 130), (128, 128)), ((3001, 2047, 4093), (64, 64)),
           ((1900, 2100, 77), (128, 128)), ((1000, 1000, 1000), (64, 64))]
 KSPLIT = {(1000, 1000, 1000)}

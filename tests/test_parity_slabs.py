@@ -1,0 +1,75 @@
+"""Slab boundaries of the two 64x64 matrix-core tiles (GPU tests).
+
+The plain 64x64 tile walks K in slabs of 16 and the two-set tile in slabs of
+32, whose two halves the two wave sets share. A product runs its whole slabs
+through the pipelined loop (the steady state needs three or more, the last two
+run without loads) and the partial last slab, if any, separately. These tests
+take K on both sides of every such boundary, up to three whole slabs plus a
+partial one, for every transpose pair:
+- small-integer operands, where every partial sum is exact and the whole of C
+  must equal the integer product bit for bit;
+- uniform operands with alpha and beta against the oracle on sampled outputs,
+  the last row and column included.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dense_fp32_matrix_sgemm_amd as sg
+import oracle
+import synth
+from oracle.check import assert_within
+from tests.gpu_util import gemm_ex
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(False, False), (False, True), (True, False), (True, True)]
+
+# (M, N), the slab depth of the tile the library picks for it, and the K
+# values around its boundaries: 1, under and over one slab, two, three, four.
+TILES = [((1536, 1500), 16), ((1000, 1000), 32)]
+
+
+def _ks(bk):
+    return sorted({1, bk // 2, bk - 1, bk, bk + 1, 2 * bk - 1, 2 * bk, 2 * bk + 1, 3 * bk, 3 * bk + 1, 4 * bk - 1,
+                   4 * bk + 5})
+
+
+CASES = [(mn, bk, k) for mn, bk in TILES for k in _ks(bk)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sg.load_library()
+
+
+def _stored(x, trans):
+    return np.ascontiguousarray(x.T) if trans else x
+
+
+@pytest.mark.parametrize("mn,bk,K", CASES, ids=[f"{m}x{n}x{k}" for (m, n), _, k in CASES])
+def test_slab_boundaries(mn, bk, K):
+    M, N = mn
+    shape = sg.sgemm_mfma_shape(M, N)
+    assert shape[:3] == (64, 64, bk), shape
+    for tA, tB in PAIRS:
+        print(f"[slabs] {M}x{N}x{K} tile {shape} pair {(tA, tB)}", flush=True)
+        Ai = synth.small_int(K + 31, (M, K))
+        Bi = synth.small_int(K + 32, (K, N))
+        Ci = gemm_ex(tA, tB, 1.0, _stored(Ai, tA), _stored(Bi, tB), 0.0, np.zeros((M, N), np.float32), "mfma")
+        exact = Ai.astype(np.int64) @ Bi.astype(np.int64)
+        assert np.array_equal(Ci.astype(np.int64), exact), (M, N, K, tA, tB)
+
+        opA = synth.uniform_pm1(K + 33, (M, K))
+        opB = synth.uniform_pm1(K + 34, (K, N))
+        C0 = synth.uniform_pm1(K + 35, (M, N))
+        A, B = _stored(opA, tA), _stored(opB, tB)
+        C = gemm_ex(tA, tB, 0.75, A, B, -0.5, C0, "mfma")
+        rng = np.random.default_rng(K)
+        rows = np.concatenate([rng.integers(0, M, 1500), np.full(N, M - 1), np.arange(M)])
+        cols = np.concatenate([rng.integers(0, N, 1500), np.arange(N), np.full(M, N - 1)])
+        want, S = oracle.gemm_ex_entries(tA, tB, 0.75, A, B, -0.5, C0, rows, cols)
+        assert_within(C[rows, cols], want, S, f"{M}x{N}x{K} {(tA, tB)}")
