@@ -739,6 +739,10 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
     using OpB = typename T::OpB;
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::kThreads;
     constexpr int GW = Cfg::kGroupsPerWave;
+    // The steady loop reads the next slab's first group into fragment slot 0
+    // before it multiplies this slab's last group, so that group must sit in
+    // slot 1: an even number of groups per wave.
+    static_assert(GW % 2 == 0, "the pipelined loop needs an even number of k-groups per wave");
     constexpr int CA = OpA::kChunks, CB = OpB::kChunks;
     constexpr int NS = Cfg::WAVES_M * Cfg::WAVES_N;  // waves per set
 
