@@ -86,6 +86,25 @@ def test_lp_small_integers_bit_exact(dtype, pair):
         assert np.array_equal(C.astype(np.float64), want), (M, N, K)
 
 
+# The register-staged 64x64 tile (products too small to give every compute
+# unit a larger tile, such as 1000 x 1000) walks K in slabs of 64: K on both
+# sides of one to four whole slabs, with a partial one.
+LP_SLAB_KS = [1, 16, 63, 64, 65, 127, 128, 129, 192, 193, 255, 261]
+
+
+@pytest.mark.parametrize("K", LP_SLAB_KS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_small_tile_slab_boundaries(dtype, K):
+    M = N = 1000
+    for tA, tB in PAIRS:
+        print(f"[lowp] slab boundaries {dtype} {M}x{N}x{K} {(tA, tB)}", flush=True)
+        opA, opB, _ = _case(dtype, M, N, K, K + 40, dist="int")
+        C0 = synth.small_int(K + 41, (M, N))
+        C, _, _ = _run(dtype, tA, tB, 1.0, opA, opB, 0.0, C0)
+        want = opA.astype(np.float64) @ opB.astype(np.float64)
+        assert np.array_equal(C.astype(np.float64), want), (M, N, K, tA, tB)
+
+
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_lp_ragged_and_large_sampled(dtype, pair):
