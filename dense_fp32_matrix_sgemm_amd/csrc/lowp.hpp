@@ -221,6 +221,9 @@ __device__ __forceinline__ void lp_tile(const LpProblem &p, int tm, int tn, shor
     using OpA = LpOperand<BM, Cfg::WM, BK, NT, !TA>;
     using OpB = LpOperand<BN, Cfg::WN, BK, NT, TB>;
     constexpr int G = BK / 16;  // steps of 16 k per slab
+    // The steady loop reads the next slab's step 0 into fragment slot 0 before
+    // it multiplies this slab's last step from slot (G - 1) & 1: an even G.
+    static_assert(G % 2 == 0, "the pipelined slab loop needs an even number of steps of 16 k");
     constexpr int CA = OpA::kChunks, CB = OpB::kChunks;
     constexpr int NA = OpA::NB, NBl = OpB::NB;
 
@@ -396,9 +399,21 @@ constexpr int lp_lds_elems()
                 LpOperand<Cfg::BN, Cfg::WN, Cfg::BK, Cfg::kThreads, TB>::kElems);
 }
 
+// Waves per SIMD a work-group of this kernel can have resident: the tile's
+// register budget (Cfg::kWavesPerEU), or fewer where its two LDS stages
+// leave room for fewer work-groups in a compute unit's 160 KiB.
+template <class Cfg, bool TA, bool TB>
+constexpr int lp_waves_per_eu()
+{
+    constexpr int kLdsPerCu = 160 * 1024;
+    constexpr int wg_per_cu = kLdsPerCu / (int(sizeof(short)) * lp_lds_elems<Cfg, TA, TB>());
+    constexpr int by_lds = wg_per_cu * (Cfg::kThreads / 64) / 4;
+    return by_lds < 1 ? 1 : by_lds < Cfg::kWavesPerEU ? by_lds : Cfg::kWavesPerEU;
+}
+
 template <class Cfg, LpType T, bool TA, bool TB>
 __global__ __launch_bounds__(Cfg::kThreads)
-__attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerEU, Cfg::kWavesPerEU))) void lp_tiles_kernel(LpProblem p, int tiles_m)
+__attribute__((amdgpu_waves_per_eu(lp_waves_per_eu<Cfg, TA, TB>(), lp_waves_per_eu<Cfg, TA, TB>()))) void lp_tiles_kernel(LpProblem p, int tiles_m)
 {
     __shared__ __attribute__((aligned(16))) short lds[lp_lds_elems<Cfg, TA, TB>()];
     int tm, tn;

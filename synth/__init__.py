@@ -22,11 +22,12 @@ Value maps (all results are exactly representable in float32):
   bits) or f16 (11) hold exactly, for the reduced-precision workload;
   ``to_lowp_bits`` gives their 16-bit encodings.
 
-The pages seed a uniform generator (P1 "Naive Implementation": seed 42 and
-rand()/RAND_MAX over [0, 1]; "From 306 ms to 86 ms", "How each kernel was
-timed": the same seeded random matrices for every kernel). glibc's rand() is
-not portable, so the distribution is kept and the generator replaced; the
-2**-24 grid keeps every product of two inputs exact in double precision.
+The pages draw their inputs from a seeded uniform generator ("Matrix
+Multiplication -- Naive to Tiled", section 02: seed 42, rand()/RAND_MAX on
+[0, 1]), and time every kernel on identical seeded inputs ("From 306 ms to
+86 ms", "How each kernel was timed"). glibc's rand() is not portable, so the
+distribution is kept and the generator replaced; the 2**-24 grid keeps every
+product of two inputs exact in double precision.
 """
 
 from __future__ import annotations

@@ -96,6 +96,11 @@ LP_SLAB_KS = [1, 16, 63, 64, 65, 127, 128, 129, 192, 193, 255, 261]
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_lp_small_tile_slab_boundaries(dtype, K):
     M = N = 1000
+    # The 16-bit launch takes the largest of its 256x256, 128x128 and 64x64
+    # tiles whose count reaches the compute units (256 on MI355X): 1000 x 1000
+    # has 16 and 64 of the larger two, so it runs the 64x64 tile with slabs of 64.
+    tiles = lambda t: -(-M // t) * -(-N // t)
+    assert tiles(256) < 256 and tiles(128) < 256
     for tA, tB in PAIRS:
         print(f"[lowp] slab boundaries {dtype} {M}x{N}x{K} {(tA, tB)}", flush=True)
         opA, opB, _ = _case(dtype, M, N, K, K + 40, dist="int")
