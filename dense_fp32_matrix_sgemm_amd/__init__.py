@@ -65,8 +65,12 @@ SGEMM_NAIVE = 0
 SGEMM_TILED = 1
 SGEMM_REGBLOCK = 2
 SGEMM_MFMA = 3
+SGEMM_TILED_T8 = 4
+SGEMM_TILED_T16 = 5
+SGEMM_TILED_T32 = 6
 VARIANTS = {"best": SGEMM_BEST, "naive": SGEMM_NAIVE, "tiled": SGEMM_TILED,
-            "regblock": SGEMM_REGBLOCK, "mfma": SGEMM_MFMA}
+            "regblock": SGEMM_REGBLOCK, "mfma": SGEMM_MFMA,
+            "tiled8": SGEMM_TILED_T8, "tiled16": SGEMM_TILED_T16, "tiled32": SGEMM_TILED_T32}
 
 # Symbols the shared library exports (the functions of include/sgemm.h).
 EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args", "sgemm_ex_ws", "sgemm_ex_ws_check_args",

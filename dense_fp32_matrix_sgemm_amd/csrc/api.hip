@@ -15,12 +15,14 @@ namespace {
 // Per-device cache: 0 = not yet asked, -1 = not a gfx950, otherwise the
 // device's compute-unit count. Written once per device; racing writers store
 // the same value.
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_device_cus[kMaxDevices];
+std::atomic<int> g_device_cus[sgemm_impl::kMaxDevices];
+
+}  // namespace
 
 // Compute units of the current device if it is a gfx950, else 0.
-int current_gfx950_cus()
+int sgemm_impl::current_gfx950_cus()
 {
+    using sgemm_impl::kMaxDevices;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
     if (dev >= kMaxDevices) return 0;
@@ -36,6 +38,9 @@ int current_gfx950_cus()
     }
     return state > 0 ? state : 0;
 }
+
+namespace {
+using sgemm_impl::current_gfx950_cus;
 
 hipError_t launch_mfma(const sgemm_impl::Problem &p, hipStream_t s)
 {
@@ -103,7 +108,10 @@ extern "C" int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha
     } else {
         switch (variant) {
         case SGEMM_NAIVE: err = sgemm_impl::launch_naive(p, s); break;
-        case SGEMM_TILED: err = sgemm_impl::launch_tiled(p, s); break;
+        case SGEMM_TILED: err = sgemm_impl::launch_tiled(p, 0, s); break;
+        case SGEMM_TILED_T8: err = sgemm_impl::launch_tiled(p, 8, s); break;
+        case SGEMM_TILED_T16: err = sgemm_impl::launch_tiled(p, 16, s); break;
+        case SGEMM_TILED_T32: err = sgemm_impl::launch_tiled(p, 32, s); break;
         case SGEMM_REGBLOCK: err = sgemm_impl::launch_regblock(p, s); break;
         case SGEMM_MFMA: err = launch_mfma(p, s); break;
         default: return SGEMM_ERR_VARIANT;

@@ -26,7 +26,7 @@ Span span_of(const void *p, int rows, int cols, int ld, std::size_t elem = sizeo
 
 bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
-bool known_variant(int v) { return v >= SGEMM_BEST && v <= SGEMM_MFMA; }
+bool known_variant(int v) { return v >= SGEMM_BEST && v <= SGEMM_TILED_T32; }
 
 bool known_op(int op) { return op == SGEMM_OP_N || op == SGEMM_OP_T; }
 
@@ -131,6 +131,9 @@ extern "C" const char *sgemm_variant_name(int variant)
     case SGEMM_TILED: return "tiled";
     case SGEMM_REGBLOCK: return "regblock";
     case SGEMM_MFMA: return "mfma";
+    case SGEMM_TILED_T8: return "tiled8";
+    case SGEMM_TILED_T16: return "tiled16";
+    case SGEMM_TILED_T32: return "tiled32";
     default: return nullptr;
     }
 }

@@ -30,7 +30,10 @@ struct Problem {
 // launch status; the problem has already been validated and has work to do:
 // M > 0, N > 0, K > 0 and alpha != 0 (the other cases only scale C).
 hipError_t launch_naive(const Problem &p, hipStream_t stream);
-hipError_t launch_tiled(const Problem &p, hipStream_t stream);
+// The tiled rung with T x T tiles, T in {8, 16, 32}; T = 0 takes
+// tiled_tile_size(M, N), the tile the rung picks for the shape.
+hipError_t launch_tiled(const Problem &p, int T, hipStream_t stream);
+int tiled_tile_size(int M, int N);
 hipError_t launch_regblock(const Problem &p, hipStream_t stream);
 hipError_t launch_mfma_nn(const Problem &p, hipStream_t stream);  // one per transpose pair
 hipError_t launch_mfma_nt(const Problem &p, hipStream_t stream);
@@ -68,18 +71,26 @@ struct LpProblem {
 hipError_t launch_lowp_bf16(const LpProblem &p, hipStream_t stream);
 hipError_t launch_lowp_f16(const LpProblem &p, hipStream_t stream);
 
+// Devices the per-device caches cover (device ordinals 0 .. kMaxDevices-1).
+constexpr int kMaxDevices = 64;
+// Compute units of the calling thread's current device if it is a gfx950,
+// else 0 (also for an ordinal past kMaxDevices). Cached per device.
+int current_gfx950_cus();
+
 // Largest grid extent used along y (row blocks); kernels loop over the rest.
 constexpr unsigned kMaxGridY = 65535;
 
 // Splits a product over a 1-D grid of BM x BN tiles into bands of at most
-// 2^22 tiles each (far inside the grid limit) and calls launch(sub, tiles_m,
-// tiles_n) for each band. A band is itself a product: op(A) and C start at
-// its first row, op(B) and C at its first column. Band edges fall on
-// multiples of BM and BN, so 16-byte alignment of the operands carries over.
+// max_tiles tiles each (2^22 by default, far inside the grid limit; work-group
+// size times max_tiles must stay under 2^32 work-items) and calls
+// launch(sub, tiles_m, tiles_n) for each band. A band is itself a product:
+// op(A) and C start at its first row, op(B) and C at its first column. Band
+// edges fall on multiples of BM and BN, so 16-byte alignment of the operands
+// carries over.
 template <int BM, int BN, class Launch>
-hipError_t for_each_band(const Problem &p, Launch &&launch)
+hipError_t for_each_band(const Problem &p, Launch &&launch, std::int64_t max_tiles = std::int64_t(1) << 22)
 {
-    constexpr std::int64_t kMaxTiles = std::int64_t(1) << 22;
+    const std::int64_t kMaxTiles = max_tiles;
     const std::int64_t tiles_n_all = (std::int64_t(p.N) + BN - 1) / BN;
     const std::int64_t band_tn = tiles_n_all < kMaxTiles ? tiles_n_all : kMaxTiles;
     const std::int64_t band_tm = kMaxTiles / band_tn;

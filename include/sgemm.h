@@ -66,8 +66,11 @@ typedef enum sgemm_op {
 /* Kernel variants: the ladder from the pages' naive kernel to matrix cores.
  *  NAIVE    one work-item per element of C, operands straight from global
  *           memory ("Matrix Multiplication -- Naive to Tiled", section 02).
- *  TILED    16 x 16 tiles of A and B staged in LDS, zero-filled at the edges,
- *           two barriers per K step (same page, sections 04-05).
+ *  TILED    T x T tiles of A and B staged in LDS, zero-filled at the edges,
+ *           two barriers per K step (same page, sections 04-05), with the
+ *           tile size T chosen per shape from 8, 16 and 32 (same page,
+ *           exercise 2; "Naive GEMM vs Tiled GEMM", the kernel with 32 x 32
+ *           tiles). TILED_T8, TILED_T16 and TILED_T32 fix T.
  *  REGBLOCK 128 x 128 LDS tiles, an 8 x 8 block of C per work-item in
  *           registers, 128-bit global loads, double-buffered LDS (same page,
  *           section 07; "From 306 ms to 86 ms", "Register blocking").
@@ -80,7 +83,10 @@ typedef enum sgemm_variant {
     SGEMM_NAIVE = 0,
     SGEMM_TILED = 1,
     SGEMM_REGBLOCK = 2,
-    SGEMM_MFMA = 3
+    SGEMM_MFMA = 3,
+    SGEMM_TILED_T8 = 4,
+    SGEMM_TILED_T16 = 5,
+    SGEMM_TILED_T32 = 6
 } sgemm_variant;
 
 /*

@@ -35,7 +35,8 @@ int main()
     const int sizes[] = {INT_MIN, -7, -1, 0, 1, 3, 4, 7, 8, 31, 64, 255, 256, 4093, 4096, 46400, 65600, 1 << 30,
                          INT_MAX};
     const int lds[] = {INT_MIN, -1, 0, 1, 4, 8, 4096, 4100, INT_MAX};
-    const int variants[] = {-2, SGEMM_BEST, SGEMM_NAIVE, SGEMM_TILED, SGEMM_REGBLOCK, SGEMM_MFMA, 4, INT_MAX};
+    const int variants[] = {-2, SGEMM_BEST, SGEMM_NAIVE, SGEMM_TILED, SGEMM_REGBLOCK, SGEMM_MFMA, SGEMM_TILED_T8,
+                            SGEMM_TILED_T16, SGEMM_TILED_T32, 7, INT_MAX};
 
     // Plain and general argument checks: every combination returns a status,
     // and the status string exists.
@@ -64,9 +65,9 @@ int main()
     for (int v : variants) {
         const int s = sgemm_check_args(8, 8, 8, fake(a), 8, fake(b), 8, fake(c), 8, v);
         expect(is_status(s), "variant status", v);
-        expect((v >= SGEMM_BEST && v <= SGEMM_MFMA) == (s == SGEMM_OK), "variant validity", v, s);
+        expect((v >= SGEMM_BEST && v <= SGEMM_TILED_T32) == (s == SGEMM_OK), "variant validity", v, s);
         const char *name = sgemm_variant_name(v);
-        expect((name != nullptr) == (v >= SGEMM_BEST && v <= SGEMM_MFMA), "variant name", v);
+        expect((name != nullptr) == (v >= SGEMM_BEST && v <= SGEMM_TILED_T32), "variant name", v);
     }
     for (int s = -20; s <= 5; ++s) expect(sgemm_status_string(s) != nullptr, "status string of any code", s);
 

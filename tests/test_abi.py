@@ -49,7 +49,7 @@ def test_status_strings(lib):
 def test_variant_names(lib):
     for name, code in sg.VARIANTS.items():
         assert sg.sgemm_variant_name(code) == name
-    assert sg.sgemm_variant_name(4) is None
+    assert sg.sgemm_variant_name(7) is None
     assert sg.sgemm_variant_name(-2) is None
     assert sg.sgemm_best_variant(4096, 4096, 4096) in (0, 1, 2, 3)
 
@@ -64,8 +64,9 @@ CASES = [
     ((4, 4, 4, A, 4, B, 4, C, 3, 0), sg.SGEMM_ERR_LD),
     ((4, 4, 0, A, 0, B, 4, C, 4, 0), sg.SGEMM_ERR_LD),      # lda >= max(1, K)
     ((0, 0, 0, None, 1, None, 1, None, 1, 0), sg.SGEMM_OK),  # empty, NULLs fine
-    ((4, 4, 4, A, 4, B, 4, C, 4, 4), sg.SGEMM_ERR_VARIANT),
+    ((4, 4, 4, A, 4, B, 4, C, 4, 7), sg.SGEMM_ERR_VARIANT),
     ((4, 4, 4, A, 4, B, 4, C, 4, -2), sg.SGEMM_ERR_VARIANT),
+    ((4, 4, 4, A, 4, B, 4, C, 4, 6), sg.SGEMM_OK),          # tiled rung with T = 32
     ((0, 4, 4, A, 4, B, 4, C, 4, 7), sg.SGEMM_ERR_VARIANT),  # variant checked first
     ((0, 4, 4, None, 4, None, 4, None, 4, 3), sg.SGEMM_OK),  # M == 0
     ((4, 0, 4, None, 4, None, 1, None, 1, 3), sg.SGEMM_OK),  # N == 0
