@@ -24,7 +24,11 @@ Also reported:
                 accumulation) on the same sizes, against the 16-bit matrix
                 peak, with sampled elements checked against the oracle;
   check         sampled elements compared with the oracle, and the
-                whole-matrix sum of C in double.
+                whole-matrix sum of C in double;
+  configs       the same entry point and variant on the other workloads of
+                the configuration table (128^3, 1024^3, 2048^3 and the ragged
+                3001 x 2047 x 4093 on U[-1, 1)): mean per-launch time,
+                TFLOP/s, fraction of peak and a sampled oracle check each.
 
 With --cold it instead times the product with the caches flushed by a 512 MiB
 write before every launch, next to the same launches back to back.
@@ -169,19 +173,48 @@ def cpu_baseline(A, B, target_s: float):
     t0 = time.perf_counter()
     oracle.gemm(np.ascontiguousarray(A[:rows]), B)
     dt = time.perf_counter() - t0
-    return {
+    out = {
         "value": round(flops(rows, N, K) / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product "
                   f"({rows / M:.3f} of its work), {dt:.1f} s",
+        "cpu_model": cpu_model(),
     }
+    # The same oracle on one host thread at the two smaller square sizes.
+    one = {}
+    for n in (128, 1024):
+        try:
+            s1 = oracle_seconds_one_thread(n, n, n, "u01")
+        except Exception as e:  # a baseline only: report, do not fail the bench
+            one[f"{n}^3"] = {"error": str(e)[:200]}
+            continue
+        one[f"{n}^3"] = {"seconds": round(s1, 4), "TFLOP/s": round(flops(n, n, n) / s1 / 1e12, 6)}
+    out["one_thread"] = one
+    return out
+
+
+def cpu_model() -> str | None:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # The method's configuration table: (M, N, K, value distribution).
 CONFIGS = [(128, 128, 128, "u01"), (1024, 1024, 1024, "u01"), (2048, 2048, 2048, "u01"),
            (4096, 4096, 4096, "u01"), (3001, 2047, 4093, "pm1")]
+
+
+# Variants timed by --all-configs: the four rungs (the tiled one with the tile
+# size it picks for the shape) and the tiled rung at each fixed T.
+ALL_CONFIG_VARIANTS = ("naive", "tiled", "tiled8", "tiled16", "tiled32", "regblock", "mfma")
 
 
 def read_sclk():
@@ -233,7 +266,7 @@ def all_configs(lib, sg, dev) -> dict:
         cols = np.concatenate([[N - 1, 0], rng.integers(0, N, 1022)])
         ref, sabs = oracle.gemm_entries(A, B, rows, cols)
         entry = {"M": M, "N": N, "K": K, "values": dist, "variants": {}}
-        for name in ("naive", "tiled", "regblock", "mfma"):
+        for name in ALL_CONFIG_VARIANTS:
             code = sg.VARIANTS[name]
 
             def call(code=code):
@@ -298,19 +331,77 @@ def all_configs(lib, sg, dev) -> dict:
     return result
 
 
+def config_sweep(lib, sg, dev, variant: int) -> dict:
+    """The product on the other workloads of the configuration table, through
+    the same entry point and variant as the headline: per-launch HIP-event
+    times of back-to-back launches (warm-up first), and 1024 sampled elements
+    (the four corners included) checked against the oracle."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    from oracle.check import excess, within
+    stream = torch.cuda.current_stream()
+    out = {}
+    for (M, N, K, dist) in CONFIGS:
+        if (M, N, K) == (4096, 4096, 4096):
+            continue  # the headline
+        A, B = synth.operands(M, N, K, dist)
+        dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        dC = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+        resolved = sg.sgemm_best_variant(M, N, K) if variant == sg.SGEMM_BEST else variant
+
+        def call():
+            rc = lib.sgemm(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, stream.cuda_stream,
+                           variant)
+            if rc != 0:
+                raise sg.SgemmError(rc)
+        call()
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(M + 2 * N + 3 * K)
+        rows = np.concatenate([[0, 0, M - 1, M - 1], rng.integers(0, M, 1020)])
+        cols = np.concatenate([[0, N - 1, 0, N - 1], rng.integers(0, N, 1020)])
+        ref, sabs = oracle.gemm_entries(A, B, rows, cols)
+        got = dC.cpu().numpy()[rows, cols]
+        t0 = time.perf_counter()
+        call()
+        torch.cuda.synchronize()
+        one = time.perf_counter() - t0
+        reps = int(max(50, min(2000, 0.2 / max(one, 1e-6))))
+        _, per = time_launches(call, reps, 20)
+        mean, med = sum(per) / len(per), float(np.median(per))
+        f = flops(M, N, K)
+        tf = f / (mean / 1e3) / 1e12
+        key = f"{M}x{N}x{K}"
+        out[key] = {"values": dist, "variant": sg.sgemm_variant_name(resolved), "reps": reps,
+                    "kernel_ms_mean": round(mean, 5), "kernel_ms_median": round(med, 5),
+                    "TFLOP/s": round(tf, 3), "frac": round(tf / PEAK_FP32_TFLOPS, 4),
+                    "check_sampled_elements": int(rows.size),
+                    "check_worst_error_over_bound": round(float(excess(got, ref, sabs).max()), 4),
+                    "check_pass": bool(within(got, ref, sabs).all())}
+        if resolved == sg.SGEMM_MFMA:
+            out[key]["mfma_tile"] = "x".join(str(v) for v in sg.sgemm_mfma_shape(M, N)[:3])
+        log(f"config {key}: {mean:.4f} ms mean, {tf:.2f} TFLOP/s, check {out[key]['check_worst_error_over_bound']}")
+        del dA, dB, dC
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--variant", default="best",
-                    choices=["best", "naive", "tiled", "regblock", "mfma"])
+                    choices=["best", "naive", "tiled", "tiled8", "tiled16", "tiled32", "regblock", "mfma"])
     ap.add_argument("--size", type=int, default=4096, help="M = N = K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ladder", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-general-form", action="store_true")
     ap.add_argument("--no-lowp", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads of the configuration table")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget of the CPU-baseline sample")
     ap.add_argument("--all-configs", action="store_true",
@@ -460,7 +551,7 @@ def main(argv=None) -> int:
 
     if not args.no_check:
         import oracle
-        from oracle.check import excess
+        from oracle.check import excess, within
         torch.cuda.synchronize()
         C = dC.cpu().numpy()
         rng = np.random.default_rng(1)
@@ -471,13 +562,16 @@ def main(argv=None) -> int:
         out["check"] = {
             "sampled_elements": int(rows.size),
             "worst_error_over_bound": round(worst, 4),
-            "pass": bool(worst <= 1.0),
+            "pass": bool(within(C[rows, cols], ref, sabs).all()),
             "checksum_sum_C_double": float(C.astype(np.float64).sum()),
         }
         log(f"check: {rows.size} sampled elements, worst error {worst:.3f} of bound")
 
     if ladder is not None:
         out["ladder"] = ladder
+
+    if not args.no_configs:
+        out["configs"] = config_sweep(lib, sg, dev, variant)
 
     if not args.no_general_form:
         # Same sizes, stored transposed where the pair says so; alpha = 1.
