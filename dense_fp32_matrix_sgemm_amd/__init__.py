@@ -13,6 +13,11 @@ Raw entry points (same names and arguments as the C ABI):
              stream, variant) -> status
     sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
                         C, ldc, variant) -> status
+    sgemm_ex_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
+                     C, ldc, stream, variant) -> status
+                                 (scratch in the library's static buffer)
+    sgemm_ex_noalloc_check_args(..., variant, cus) -> status
+    sgemm_ex_noalloc_scratch_bytes() -> int
     sgemm_lp(dtype, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
              ldc, stream) -> status      (A, B: bf16 or f16 encodings)
     sgemm_lp_check_args(dtype, transA, transB, M, N, K, alpha, A, lda, B,
@@ -49,6 +54,7 @@ SGEMM_ERR_DEVICE = -6
 SGEMM_ERR_ALIAS = -7
 SGEMM_ERR_OP = -8
 SGEMM_ERR_DTYPE = -9
+SGEMM_ERR_SCRATCH = -10
 
 # 16-bit operand types (sgemm_lp_type).
 SGEMM_LP_BF16 = 1
@@ -74,7 +80,8 @@ VARIANTS = {"best": SGEMM_BEST, "naive": SGEMM_NAIVE, "tiled": SGEMM_TILED,
 
 # Symbols the shared library exports (the functions of include/sgemm.h).
 EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args", "sgemm_ex_ws", "sgemm_ex_ws_check_args",
-           "sgemm_ex_workspace_size", "sgemm_lp", "sgemm_lp_check_args", "sgemm_status_string", "sgemm_variant_name",
+           "sgemm_ex_workspace_size", "sgemm_ex_noalloc", "sgemm_ex_noalloc_check_args",
+           "sgemm_ex_noalloc_scratch_bytes", "sgemm_lp", "sgemm_lp_check_args", "sgemm_status_string", "sgemm_variant_name",
            "sgemm_best_variant", "sgemm_mfma_tile", "sgemm_mfma_shape")
 
 _lib = None
@@ -116,6 +123,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_ex_ws_check_args.restype = i
     lib.sgemm_ex_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.sgemm_ex_workspace_size.restype = sz
+    lib.sgemm_ex_noalloc.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp, i]
+    lib.sgemm_ex_noalloc.restype = i
+    lib.sgemm_ex_noalloc_check_args.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, i, i]
+    lib.sgemm_ex_noalloc_check_args.restype = i
+    lib.sgemm_ex_noalloc_scratch_bytes.argtypes = []
+    lib.sgemm_ex_noalloc_scratch_bytes.restype = sz
     lib.sgemm_lp.argtypes = [i, i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp]
     lib.sgemm_lp.restype = i
     lib.sgemm_lp_check_args.argtypes = [i, i, i, i, i, i, f, vp, i, vp, i, f, vp, i]
@@ -159,6 +172,22 @@ def sgemm_ex_ws_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
                            variant) -> int:
     return load_library().sgemm_ex_ws_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                                  workspace, workspace_bytes, variant)
+
+
+def sgemm_ex_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant) -> int:
+    return load_library().sgemm_ex_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                                           variant)
+
+
+def sgemm_ex_noalloc_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant,
+                                cus) -> int:
+    return load_library().sgemm_ex_noalloc_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                                      variant, cus)
+
+
+def sgemm_ex_noalloc_scratch_bytes() -> int:
+    """Bytes of the static device buffer sgemm_ex_noalloc works in."""
+    return int(load_library().sgemm_ex_noalloc_scratch_bytes())
 
 
 def sgemm_ex_workspace_size(transA: int, transB: int, M: int, N: int, K: int, cus: int = 0) -> int:

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(LIBDIR, "libsgemm.so")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["api.hip", "naive.hip", "tiled.hip", "regblock.hip", "scale.hip",
-               "mfma_nn.hip", "mfma_nt.hip", "mfma_tn.hip", "mfma_tt.hip", "lowp_bf16.hip", "lowp_f16.hip"]
+               "mfma_nn.hip", "mfma_nt.hip", "mfma_tn.hip", "mfma_tt.hip", "lowp_bf16.hip", "lowp_f16.hip", "noalloc.hip"]
 CXX_SOURCES = ["args.cpp", "select.cpp"]
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

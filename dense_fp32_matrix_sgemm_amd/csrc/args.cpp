@@ -5,6 +5,7 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "select.hpp"
 #include "sgemm.h"
 
 namespace {
@@ -119,6 +120,7 @@ extern "C" const char *sgemm_status_string(int status)
     case SGEMM_ERR_ALIAS: return "C overlaps A or B";
     case SGEMM_ERR_OP: return "transpose flag is neither SGEMM_OP_N nor SGEMM_OP_T";
     case SGEMM_ERR_DTYPE: return "16-bit operand type is neither SGEMM_LP_BF16 nor SGEMM_LP_F16";
+    case SGEMM_ERR_SCRATCH: return "the product needs more scratch than the library's static buffer holds";
     default: return "unknown status";
     }
 }
@@ -145,3 +147,18 @@ extern "C" int sgemm_best_variant(int M, int N, int K)
     (void)K;
     return SGEMM_MFMA;
 }
+
+extern "C" int sgemm_ex_noalloc_check_args(int transA, int transB, int M, int N, int K, float alpha,
+                                           const float *A, int lda, const float *B, int ldb, float beta,
+                                           const float *C, int ldc, int variant, int cus)
+{
+    const int rc = sgemm_ex_check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant);
+    if (rc != SGEMM_OK || M == 0 || N == 0 || K == 0 || alpha == 0.0f) return rc;
+    const int v = variant == SGEMM_BEST ? sgemm_best_variant(M, N, K) : variant;
+    if (v != SGEMM_MFMA) return SGEMM_OK;  // only the split schedule uses scratch
+    if (sgemm_ex_workspace_size(transA, transB, M, N, K, cus) > sgemm_impl::kNoallocScratchBytes)
+        return SGEMM_ERR_SCRATCH;
+    return SGEMM_OK;
+}
+
+extern "C" size_t sgemm_ex_noalloc_scratch_bytes(void) { return sgemm_impl::kNoallocScratchBytes; }

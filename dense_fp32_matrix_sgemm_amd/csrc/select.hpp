@@ -25,4 +25,9 @@ SplitChoice choose_split(int M, int N, int K, int cus);
 // Workspace of the split schedule: two partial tiles per work-group.
 std::size_t split_workspace_bytes(MfmaTile tile, int grid);
 
+// Size of the library's own static scratch buffer (sgemm_ex_noalloc): the
+// largest workspace the split schedule asks for on a 256-CU MI355X (one
+// 256 x 256 work-group per compute unit, two partial tiles each).
+constexpr std::size_t kNoallocScratchBytes = std::size_t(128) << 20;
+
 }  // namespace sgemm_impl

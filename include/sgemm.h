@@ -25,7 +25,8 @@
  * call (sgemm_ex_ws works in scratch memory the caller passes), keeps no
  * pointer after returning and has no mutable global state besides a
  * per-device cache of the device's architecture, so calls from several host
- * threads are safe.
+ * threads are safe. The one exception is sgemm_ex_noalloc, which works in a
+ * static device buffer of the library's own (see there).
  */
 #ifndef SGEMM_H
 #define SGEMM_H
@@ -48,7 +49,9 @@ typedef enum sgemm_status {
     SGEMM_ERR_DEVICE = -6,   /* no usable HIP device, or it is not gfx950        */
     SGEMM_ERR_ALIAS = -7,    /* C's extent overlaps A's or B's                   */
     SGEMM_ERR_OP = -8,       /* transpose flag not SGEMM_OP_N or SGEMM_OP_T      */
-    SGEMM_ERR_DTYPE = -9     /* 16-bit type not SGEMM_LP_BF16 or SGEMM_LP_F16    */
+    SGEMM_ERR_DTYPE = -9,    /* 16-bit type not SGEMM_LP_BF16 or SGEMM_LP_F16    */
+    SGEMM_ERR_SCRATCH = -10  /* sgemm_ex_noalloc: the product needs more scratch
+                                than the library's static buffer holds          */
 } sgemm_status;
 
 /* 16-bit operand types of sgemm_lp. */
@@ -247,6 +250,54 @@ int sgemm_ex_ws_check_args(int transA, int transB, int M, int N, int K,
  * be as fast, or the arguments are invalid). Pure host logic: no HIP call.
  */
 size_t sgemm_ex_workspace_size(int transA, int transB, int M, int N, int K, int cus);
+
+/*
+ * sgemm_ex_ws without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the split schedule's partial tiles go to a static
+ * device buffer the library holds, sgemm_ex_noalloc_scratch_bytes() bytes
+ * (128 MiB: the largest workspace the split schedule asks for on a 256-CU
+ * MI355X) on each GPU the library runs on, from when the library's code is
+ * loaded on that GPU until the process ends. The call itself allocates
+ * nothing and calls no allocating routine.
+ *
+ * Arguments and behaviour: those of sgemm_ex (same checks, same order), and
+ * the same product as sgemm_ex_ws given a large enough workspace: the same
+ * plan, kernels and bits. After the checks, a product that the matrix-core
+ * variant (or SGEMM_BEST) would put on the split schedule with more scratch
+ * than the buffer holds returns SGEMM_ERR_SCRATCH without launching anything
+ * (not on a 256-CU MI355X, where every plan fits). The first call on a device
+ * looks up that device's address of the buffer (SGEMM_ERR_DEVICE if that
+ * fails).
+ *
+ * Every call on one GPU shares that GPU's buffer, and what a call leaves in
+ * it is never read by the next (each partial tile is written before it is
+ * read). Calls whose kernels may run at the same time on one GPU (different
+ * streams with no ordering between them) race on the buffer: order them on
+ * one stream, or use sgemm_ex_ws with a workspace per stream.
+ */
+int sgemm_ex_noalloc(int transA, int transB, int M, int N, int K,
+                     float alpha,
+                     const float *A, int lda,
+                     const float *B, int ldb,
+                     float beta,
+                     float *C, int ldc,
+                     void *stream, int variant);
+
+/* The host-side checks of sgemm_ex_noalloc() alone, for a device with `cus`
+ * compute units (cus <= 0: 256): sgemm_ex's checks, then SGEMM_ERR_SCRATCH
+ * where the product would need more than the static buffer. Makes no HIP
+ * call and touches no memory. */
+int sgemm_ex_noalloc_check_args(int transA, int transB, int M, int N, int K,
+                                float alpha,
+                                const float *A, int lda,
+                                const float *B, int ldb,
+                                float beta,
+                                const float *C, int ldc,
+                                int variant, int cus);
+
+/* Bytes of the static scratch buffer sgemm_ex_noalloc works in. */
+size_t sgemm_ex_noalloc_scratch_bytes(void);
 
 /*
  * The reduced-precision workload: the tensor-core variant "Matrix

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     codes = [sg.SGEMM_OK, sg.SGEMM_ERR_DIM, sg.SGEMM_ERR_LD, sg.SGEMM_ERR_NULL,
              sg.SGEMM_ERR_VARIANT, sg.SGEMM_ERR_LAUNCH, sg.SGEMM_ERR_DEVICE, sg.SGEMM_ERR_ALIAS,
-             sg.SGEMM_ERR_OP, sg.SGEMM_ERR_DTYPE]
+             sg.SGEMM_ERR_OP, sg.SGEMM_ERR_DTYPE, sg.SGEMM_ERR_SCRATCH]
     texts = [sg.sgemm_status_string(c) for c in codes]
     assert len(set(texts)) == len(texts)
     assert "unknown status" not in texts
@@ -350,3 +350,39 @@ def test_split_workspace_size(lib):
     assert sg.sgemm_ex_workspace_size(N_, N_, 3001, 2047, 0, 256) == 0
     assert sg.sgemm_ex_workspace_size(N_, N_, 4096, 3, 1 << 20, 256) == 0
     assert sg.sgemm_ex_workspace_size(T_, T_, 3, 4096, 1 << 20, 256) == 0
+
+
+@pytest.mark.parametrize("args,want", EX_CASES)
+def test_noalloc_checks_are_the_general_checks(lib, args, want):
+    # sgemm_ex_noalloc checks what sgemm_ex checks, in the same order.
+    assert sg.sgemm_ex_noalloc_check_args(*args, 256) == want
+
+
+@pytest.mark.parametrize("args,want", [c for c in EX_CASES if c[1] != sg.SGEMM_OK])
+def test_noalloc_rejects_before_touching_the_gpu(lib, args, want):
+    assert sg.sgemm_ex_noalloc(*args[:13], None, args[13]) == want
+
+
+def test_noalloc_scratch_limit(lib):
+    # The static buffer holds the largest split workspace on 256 compute units;
+    # a device with more would need more for some products, which is a clear
+    # error, and only where the matrix-core variant would split.
+    limit = sg.sgemm_ex_noalloc_scratch_bytes()
+    assert limit == 128 << 20 == sg.sgemm_ex_workspace_size(N_, N_, 3001, 2047, 4093, 256)
+    ragged = (N_, N_, 3001, 2047, 16384, 1.0, A, 16384, B, 2047, 0.0, C, 2047)
+    for cus in (0, 64, 128, 256):
+        assert sg.sgemm_ex_noalloc_check_args(*ragged, sg.SGEMM_MFMA, cus) == sg.SGEMM_OK
+    for cus in (512, 1024):
+        assert sg.sgemm_ex_workspace_size(N_, N_, 3001, 2047, 16384, cus) > limit
+        assert sg.sgemm_ex_noalloc_check_args(*ragged, sg.SGEMM_MFMA, cus) == sg.SGEMM_ERR_SCRATCH
+        assert sg.sgemm_ex_noalloc_check_args(*ragged, sg.SGEMM_BEST, cus) == sg.SGEMM_ERR_SCRATCH
+        for v in (sg.SGEMM_NAIVE, sg.SGEMM_TILED, sg.SGEMM_REGBLOCK):   # never split
+            assert sg.sgemm_ex_noalloc_check_args(*ragged, v, cus) == sg.SGEMM_OK
+        # Nothing to multiply: nothing to split.
+        assert sg.sgemm_ex_noalloc_check_args(*ragged[:5], 0.0, *ragged[6:], sg.SGEMM_MFMA, cus) == sg.SGEMM_OK
+    assert "scratch" in sg.sgemm_status_string(sg.SGEMM_ERR_SCRATCH)
+
+
+def test_noalloc_nothing_to_do_returns_ok_without_gpu(lib):
+    assert sg.sgemm_ex_noalloc(N_, N_, 0, 5, 5, 1.0, None, 5, None, 5, 0.0, None, 5, None, 3) == sg.SGEMM_OK
+    assert sg.sgemm_ex_noalloc(T_, N_, 4, 4, 4, 0.0, None, 4, None, 4, 1.0, C, 4, None, 3) == sg.SGEMM_OK
