@@ -120,7 +120,7 @@ template <int F, int W, int BK, int NT, bool KC_>
 struct Operand {
     static constexpr bool KC = KC_;
     static constexpr int NB = W / 32;                          // MFMA blocks per wave
-    static constexpr int TI = KC ? 1 : (W >= 128 ? 4 : W / 32);  // blocks fed by one LDS read
+    static constexpr int TI = KC ? 1 : W % 128 == 0 ? 4 : W % 64 == 0 ? 2 : 1;  // blocks fed by one LDS read
     static constexpr int NJ = NB / TI;                         // LDS reads per step (FC)
     static constexpr int kPitch = KC ? BK + 4 : F;             // LDS row pitch, floats
     static constexpr int kFloats = KC ? F * (BK + 4) : BK * F;
@@ -128,13 +128,17 @@ struct Operand {
     static constexpr int kRowLen = KC ? BK : F;                // stored row length in a tile
     static constexpr int kRowChunks = kRowLen / 4;             // 16-byte chunks per stored row
     static constexpr int kChunks = F * BK / 4 / NT;            // chunks per work-item per slab
-    static constexpr int kRowStep = NT / kRowChunks;           // stored rows between them
+    static constexpr int kThreadsPerSlab = NT;                 // work-items sharing a slab's chunks
+    // With NT a multiple of the chunks per stored row, a work-item's chunks lie
+    // kRowStep stored rows apart in one column; otherwise each has its own row
+    // and column (kEven false).
+    static constexpr bool kEven = NT % kRowChunks == 0;
+    static constexpr int kRowStep = NT / kRowChunks;           // stored rows between them (kEven)
     static constexpr int kReads = KC ? NB : 4 * NJ;            // LDS reads per group of 8 k
     using V = typename VecT<TI>::T;
     static_assert(TI == 1 || TI == 2 || TI == 4, "interleave must be 1, 2 or 4");
     static_assert(NB == NJ * TI, "wave tile must split into interleaved groups");
     static_assert(kChunks * 4 * NT == F * BK, "tile must split evenly over the work-items");
-    static_assert(NT % kRowChunks == 0, "chunk rows must advance evenly");
 
     // Free index, within the wave's W, of lane column c (0..31) of block b.
     __device__ static constexpr int free_index(int b, int c)
@@ -207,52 +211,56 @@ struct OperandRef {
 // tile body: chunk q of every slab starts at chunk(q) + slab offset. With
 // EDGE, addresses are clamped into the operand (see interior_tile) and
 // place() rotates an FC chunk read from a shifted address back into place.
+// When the work-items' chunks advance evenly (Op::kEven) one offset and one
+// shift serve every chunk; otherwise each chunk keeps its own.
 template <class Op, bool EDGE>
 struct OperandSource {
+    static constexpr bool kPerChunk = (EDGE && Op::KC) || !Op::kEven;
+    static constexpr int kOffs = kPerChunk ? Op::kChunks : 1;
+    static constexpr int kShifts = (EDGE && !Op::KC && !Op::kEven) ? Op::kChunks : 1;
     const float *base;
     std::int64_t ld;
-    std::int64_t off[EDGE && Op::KC ? Op::kChunks : 1];  // per-chunk offsets (clamped KC rows)
-    int shift;                                           // FC: elements the read was moved left
+    std::int64_t off[kOffs];  // per-chunk offsets where needed
+    int shift[kShifts];       // FC: elements the read was moved left
 
     __device__ OperandSource(const float *X, std::int64_t ld_, std::int64_t f0, std::int64_t extent, int tid)
-        : base(X), ld(ld_), shift(0)
+        : base(X), ld(ld_)
     {
-        const int r0 = Op::chunk_row(tid), c0 = Op::chunk_col(tid);
-        if constexpr (Op::KC) {  // stored rows are free indices, columns are k
-            if constexpr (EDGE) {
 #pragma unroll
-                for (int q = 0; q < Op::kChunks; ++q) {
-                    const std::int64_t f = f0 + r0 + q * Op::kRowStep;
-                    off[q] = (f < extent ? f : extent - 1) * ld + c0;
+        for (int q = 0; q < kOffs; ++q) {
+            const int c = tid + q * Op::kThreadsPerSlab;
+            const int r0 = Op::chunk_row(c), c0 = Op::chunk_col(c);
+            if constexpr (Op::KC) {  // stored rows are free indices, columns are k
+                std::int64_t f = f0 + r0;
+                if constexpr (EDGE) f = f < extent ? f : extent - 1;
+                off[q] = f * ld + c0;
+            } else {  // stored rows are k, columns are free indices
+                std::int64_t f = f0 + c0;
+                if constexpr (EDGE) {
+                    const std::int64_t last = extent - 4;  // extent >= 4
+                    const std::int64_t fr = f < last ? f : last;
+                    const std::int64_t d = f - fr;
+                    if (q < kShifts) shift[q] = int(d < 3 ? d : 3);
+                    f = fr;
                 }
-            } else {
-                off[0] = (f0 + r0) * ld + c0;
+                off[q] = std::int64_t(r0) * ld + f;
             }
-        } else {  // stored rows are k, columns are free indices
-            std::int64_t f = f0 + c0;
-            if constexpr (EDGE) {
-                const std::int64_t last = extent - 4;  // extent >= 4
-                const std::int64_t fr = f < last ? f : last;
-                const std::int64_t d = f - fr;
-                shift = int(d < 3 ? d : 3);
-                f = fr;
-            }
-            off[0] = std::int64_t(r0) * ld + f;
         }
+        if constexpr (!EDGE || Op::KC) shift[0] = 0;
     }
     __device__ const float *chunk(int q) const
     {
-        if constexpr (EDGE && Op::KC)
+        if constexpr (kPerChunk)
             return base + off[q];
         else
             return base + off[0] + std::int64_t(q) * Op::kRowStep * ld;
     }
-    // Element e of the chunk is element e + shift of what was read (the
+    // Element e of chunk q is element e + shift of what was read (the
     // elements past the operand's edge keep junk).
-    __device__ f32x4 place(f32x4 v) const
+    __device__ f32x4 place(f32x4 v, int q) const
     {
         if constexpr (EDGE && !Op::KC) {
-            const int s = shift;
+            const int s = shift[kShifts > 1 ? q : 0];
             f32x4 r;
             r[0] = s == 0 ? v[0] : s == 1 ? v[1] : s == 2 ? v[2] : v[3];
             r[1] = s == 0 ? v[1] : s == 1 ? v[2] : v[3];
@@ -543,10 +551,10 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
     auto stash = [&](int buf, int set) {
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[set][q]);
+            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[set][q], q);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[set][q]);
+            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[set][q], q);
     };
 
     typename OpA::Frag fa[2];
@@ -781,10 +789,10 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
     auto stash = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[q]);
+            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[q], q);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[q]);
+            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[q], q);
     };
     typename OpA::Frag fa[2];
     typename OpB::Frag fb[2];
@@ -930,6 +938,7 @@ using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE, SGEMM_MFMA_MID_REG_SETS>;
 // which needs the one-set register budget.
 using MidSplitCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
 using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
+using WideCfg = MfmaConfig<SGEMM_MFMA_WIDE_TILE, SGEMM_MFMA_WIDE_REG_SETS>;
 using KSplitCfg = KSplitConfig<SGEMM_MFMA_KSPLIT_TILE>;
 
 // Products too small for a single interior tile: general tiles only.
@@ -1128,6 +1137,7 @@ hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
     switch (p.tile) {
     case MfmaTile::Big: return launch_tiles<BigCfg, TA, TB>(p, stream);
     case MfmaTile::Mid: return launch_tiles<MidCfg, TA, TB>(p, stream);
+    case MfmaTile::Wide: return launch_tiles<WideCfg, TA, TB>(p, stream);
     case MfmaTile::KSplit: return launch_ksplit<KSplitCfg, TA, TB>(p, stream);
     case MfmaTile::Small: break;
     }

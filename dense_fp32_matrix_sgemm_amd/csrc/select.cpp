@@ -13,6 +13,7 @@
 // MI355X with each shape forced over a set of products (TFLOP/s over 256
 // compute units, relative to 147 for 256x256 at 4096^3): 128x128 0.91, one
 // at a time (its two staging register sets leave room for one work-group);
+// 192x128 0.93, one at a time (0.92-0.96 on products it tiles exactly);
 // 64x64 0.59, 0.72, 0.79 and 0.84 for one to four;
 // 64x64 with its K range split over two sets of waves 0.65 alone and 0.78 two
 // at a time (it takes 1024^3 from 80 to 95 TFLOP/s). (A 256x128 shape
@@ -53,6 +54,7 @@ double launch_time(const Candidate &c, std::int64_t M, std::int64_t N, std::int6
 const Candidate kCandidates[] = {
     {MfmaTile::Big, tiles::kBig[0], tiles::kBig[1], 1, {1.0, 0, 0, 0}},
     {MfmaTile::Mid, tiles::kMid[0], tiles::kMid[1], 1, {0.91, 0, 0, 0}},
+    {MfmaTile::Wide, tiles::kWide[0], tiles::kWide[1], 1, {0.93, 0, 0, 0}},
     {MfmaTile::Small, tiles::kSmall[0], tiles::kSmall[1], 4, {0.59, 0.72, 0.79, 0.84}},
     {MfmaTile::KSplit, tiles::kKSplit[0], tiles::kKSplit[1], 2, {0.65, 0.78, 0, 0}},
 };
@@ -169,6 +171,7 @@ extern "C" int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN)
     case MfmaTile::Mid: dims = tiles::kMid; break;
     case MfmaTile::Small: dims = tiles::kSmall; break;
     case MfmaTile::KSplit: dims = tiles::kKSplit; break;
+    case MfmaTile::Wide: dims = tiles::kWide; break;
     }
     *BM = dims[0];
     *BN = dims[1];
@@ -202,6 +205,7 @@ extern "C" int sgemm_mfma_shape(int M, int N, int cus, int *shape)
         dims = tiles::kKSplit;
         sets = tiles::kKSplit[5];
         break;
+    case MfmaTile::Wide: dims = tiles::kWide; break;
     }
     for (int i = 0; i < 5; ++i) shape[i] = dims[i];
     shape[5] = sets;

@@ -27,6 +27,18 @@
 #ifndef SGEMM_MFMA_MID_REG_SETS
 #define SGEMM_MFMA_MID_REG_SETS 2
 #endif
+// 192 x 128 tiles with 2 x 4 waves of 96 x 32, two staging register sets (one
+// work-group per compute unit). Products whose 128 x 128 tiles would leave the
+// compute units unevenly loaded but whose 192 x 128 tiles come out near a
+// whole number per compute unit take them: 3001 x 2047 x 4093 (16 x 16 tiles)
+// went from 116 to 132 TFLOP/s against the 64 x 64 tile, 3072 x 2048 x 4096
+// from 126 to 142 (interleaved medians on MI355X).
+#ifndef SGEMM_MFMA_WIDE_TILE
+#define SGEMM_MFMA_WIDE_TILE 192, 128, 32, 2, 4
+#endif
+#ifndef SGEMM_MFMA_WIDE_REG_SETS
+#define SGEMM_MFMA_WIDE_REG_SETS 2
+#endif
 // The small tiles take short slabs: BK = 16 here and 32 below measured 1-3.5%
 // faster than 32 and 64 on every product that uses them, and twice as long
 // lost 5-12%.
@@ -43,7 +55,7 @@
 namespace sgemm_impl {
 
 // Interior tile shape of one matrix-core launch.
-enum class MfmaTile { Big, Mid, Small, KSplit };
+enum class MfmaTile { Big, Mid, Small, KSplit, Wide };
 
 namespace tiles {
 constexpr int kGeneral[] = {SGEMM_MFMA_TILE};
@@ -51,6 +63,7 @@ constexpr int kBig[] = {SGEMM_MFMA_BIG_TILE};
 constexpr int kMid[] = {SGEMM_MFMA_MID_TILE};
 constexpr int kSmall[] = {SGEMM_MFMA_SMALL_TILE};
 constexpr int kKSplit[] = {SGEMM_MFMA_KSPLIT_TILE};
+constexpr int kWide[] = {SGEMM_MFMA_WIDE_TILE};
 }  // namespace tiles
 
 }  // namespace sgemm_impl

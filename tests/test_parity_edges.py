@@ -4,7 +4,7 @@ Tiles that cross the bottom or right edge of C run the same loop as the
 others, with their reads clamped into the operands and the partial chunk of
 a row-contiguous operand read from a shifted address and rotated into place.
 These tests run ragged products whose chosen tile shape (each of 256x256,
-128x128, 64x64 and the 64x64 tile whose slabs two wave sets share) leaves
+192x128, 128x128, 64x64 and the 64x64 tile whose slabs two wave sets share) leaves
 partial tiles on both edges, for every transpose pair, with alpha and beta,
 and the narrowest widths the clamped reads allow (4 to 7) next to the general
 path below them. Every comparison is with the
@@ -41,8 +41,9 @@ def _stored(x, trans):
 # (M, N, K) and the tile shape the library picks for it (checked on the host);
 # 1000^3 takes the two-set 64x64 tile (one tile per compute unit), with a
 # partial last slab (1000 = 31 * 32 + 8).
-RAGGED = [((5000, 3000, 333), (256, 256)), ((4300, 4300, 130), (128, 128)), ((3001, 2047, 4093), (64, 64)),
-          ((1900, 2100, 77), (128, 128)), ((1000, 1000, 1000), (64, 64))]
+RAGGED = [((5000, 3000, 333), (256, 256)), ((4300, 4300, 130), (128, 128)), ((3001, 2047, 4093), (192, 128)),
+          ((2047, 3001, 4093), (64, 64)), ((1900, 2100, 77), (128, 128)), ((1000, 1000, 1000), (64, 64)),
+          ((2900, 1910, 515), (192, 128))]
 KSPLIT = {(1000, 1000, 1000)}
 
 

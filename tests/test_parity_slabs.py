@@ -1,9 +1,11 @@
-"""Slab boundaries of the two 64x64 matrix-core tiles (GPU tests).
+"""Slab boundaries of the matrix-core tiles (GPU tests).
 
 The plain 64x64 tile walks K in slabs of 16 and the two-set tile in slabs of
-32, whose two halves the two wave sets share. A product runs its whole slabs
-through the pipelined loop (the steady state needs three or more, the last two
-run without loads) and the partial last slab, if any, separately. These tests
+32, whose two halves the two wave sets share; the 192x128 and 128x128 tiles
+walk slabs of 32 staged through two register sets, two slabs per pass of
+their unrolled loop. A product runs its whole slabs through the pipelined
+loop (the steady state needs three or more, the last ones run without loads)
+and the partial last slab, if any, separately. These tests
 take K on both sides of every such boundary, up to three whole slabs plus a
 partial one, for every transpose pair:
 - small-integer operands, where every partial sum is exact and the whole of C
@@ -26,17 +28,20 @@ pytestmark = pytest.mark.gpu
 
 PAIRS = [(False, False), (False, True), (True, False), (True, True)]
 
-# (M, N), the slab depth of the tile the library picks for it, and the K
-# values around its boundaries: 1, under and over one slab, two, three, four.
-TILES = [((1536, 1500), 16), ((1000, 1000), 32)]
+# (M, N), the tile (BM, BN, BK) the library picks for it, and the K values
+# around its slab boundaries: 1, under and over one slab, two, three, four,
+# five and six.
+TILES = [((1536, 1500), (64, 64, 16)), ((1000, 1000), (64, 64, 32)), ((3001, 2047), (192, 128, 32)),
+         ((2000, 2040), (128, 128, 32))]
 
 
-def _ks(bk):
+def _ks(tile):
+    bk = tile[2]
     return sorted({1, bk // 2, bk - 1, bk, bk + 1, 2 * bk - 1, 2 * bk, 2 * bk + 1, 3 * bk, 3 * bk + 1, 4 * bk - 1,
-                   4 * bk + 5})
+                   4 * bk + 5, 5 * bk + 3, 6 * bk})
 
 
-CASES = [(mn, bk, k) for mn, bk in TILES for k in _ks(bk)]
+CASES = [(mn, tile, k) for mn, tile in TILES for k in _ks(tile)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -50,11 +55,11 @@ def _stored(x, trans):
     return np.ascontiguousarray(x.T) if trans else x
 
 
-@pytest.mark.parametrize("mn,bk,K", CASES, ids=[f"{m}x{n}x{k}" for (m, n), _, k in CASES])
-def test_slab_boundaries(mn, bk, K):
+@pytest.mark.parametrize("mn,tile,K", CASES, ids=[f"{m}x{n}x{k}" for (m, n), _, k in CASES])
+def test_slab_boundaries(mn, tile, K):
     M, N = mn
     shape = sg.sgemm_mfma_shape(M, N)
-    assert shape[:3] == (64, 64, bk), shape
+    assert shape[:3] == tile, shape
     for tA, tB in PAIRS:
         print(f"[slabs] {M}x{N}x{K} tile {shape} pair {(tA, tB)}", flush=True)
         Ai = synth.small_int(K + 31, (M, K))

@@ -59,7 +59,7 @@ def _sampled_check(tA, tB, alpha, A, B, beta, C0, C, what):
 
 # (M, N, K): ragged edges with a K tail, an exact fit, a deep-K thin product
 # and a square one, all put on the split schedule by the library.
-SHAPES = [(3001, 2047, 4093), (3072, 2048, 4096), (1000, 1000, 8000), (1536, 1536, 1536), (517, 509, 16001)]
+SHAPES = [(2047, 3001, 4093), (2560, 2560, 2560), (1000, 1000, 8000), (1536, 1536, 1536), (517, 509, 16001)]
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
@@ -91,7 +91,7 @@ def test_split_schedule_small_integers_bit_exact(workspace):
 
 
 def test_split_schedule_repeats_and_ignores_workspace_contents(workspace):
-    M, N, K = 3001, 2047, 4093
+    M, N, K = 2047, 3001, 4093
     print("[split] repeatability", flush=True)
     A = synth.uniform_pm1(11, (M, K))
     B = synth.uniform_pm1(12, (K, N))
@@ -103,7 +103,7 @@ def test_split_schedule_repeats_and_ignores_workspace_contents(workspace):
 
 
 def test_split_schedule_writes_only_the_window(workspace):
-    M, N, K = 3001, 2047, 4093
+    M, N, K = 2047, 3001, 4093
     print("[split] window", flush=True)
     A = synth.uniform_pm1(21, (M, K))
     B = synth.uniform_pm1(22, (K, N))
@@ -118,7 +118,7 @@ def test_split_schedule_writes_only_the_window(workspace):
 
 
 def test_short_or_missing_workspace_is_exactly_sgemm_ex(workspace):
-    M, N, K = 3072, 2048, 4096
+    M, N, K = 2560, 2560, 2560
     print("[split] fallback", flush=True)
     need = _split_bytes(False, True, M, N, K)
     assert need > 0
@@ -141,10 +141,11 @@ def test_short_or_missing_workspace_is_exactly_sgemm_ex(workspace):
 
 
 def test_products_left_on_whole_tiles_are_unchanged(workspace):
-    # Where the model keeps whole tiles (here 2048^3 and 4096 x 4096 x 256),
-    # sgemm_ex_ws is sgemm_ex bit for bit.
+    # Where the model keeps whole tiles (here 2048^3, 4096 x 4096 x 256 and
+    # 3001 x 2047 x 4093, one 192 x 128 tile per compute unit), sgemm_ex_ws is
+    # sgemm_ex bit for bit.
     print("[split] whole-tile products", flush=True)
-    for (M, N, K) in [(2048, 2048, 2048), (4096, 4096, 256)]:
+    for (M, N, K) in [(2048, 2048, 2048), (4096, 4096, 256), (3001, 2047, 4093)]:
         assert _split_bytes(False, False, M, N, K) == 0
         A = synth.uniform_pm1(41, (M, K))
         B = synth.uniform_pm1(42, (K, N))
