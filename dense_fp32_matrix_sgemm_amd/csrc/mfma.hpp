@@ -276,6 +276,16 @@ struct OperandSource {
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
 
+// f(std::integral_constant<int, I>{}) for I = B .. E-1, unrolled.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // Zero accumulators.
 template <int NA, int NB>
 __device__ __forceinline__ void clear(floatx16 (&acc)[NA][NB])
@@ -725,10 +735,14 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
 // its own share (BK / 8 / KGROUPS groups of 8 k) of every slab; the sets'
 // partial tiles are summed at the end. For products with one small tile per
 // compute unit, this puts KGROUPS waves on each SIMD instead of one.
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KGROUPS_>
+// Slabs are staged global -> registers -> LDS through REG_SETS register sets:
+// slab t+1+REG_SETS is requested while slab t is multiplied.
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KGROUPS_, int REG_SETS_ = 1>
 struct KSplitConfig {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KGROUPS = KGROUPS_;
+    static constexpr int kRegSets = REG_SETS_;
+    static_assert(kRegSets >= 1 && kRegSets <= 4, "one to four staging register sets");
     static constexpr int kThreads = 64 * WAVES_M * WAVES_N * KGROUPS;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int kGroupM = SGEMM_MFMA_GROUP_M;
@@ -776,23 +790,32 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
     const OperandSource<OpB, EDGE> srcb(p.B, p.ldb, n0, p.N, tid);
     const std::int64_t slab_a = OpA::KC ? BK : BK * p.lda, slab_b = OpB::KC ? BK : BK * p.ldb;
 
-    f32x4 ra[CA], rb[CB];
-    auto fetch = [&](int slab) {
+    // Slab s is staged in register set s % RS; in the steady loop `set` is
+    // a constant after unrolling, so the sets stay in fixed registers.
+    constexpr int RS = Cfg::kRegSets;
+    f32x4 ra[RS][CA], rb[RS][CB];
+    auto fetch = [&](int slab, int set) {
         const std::int64_t ka = slab * slab_a, kb = slab * slab_b;
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            ra[q] = load16u(srca.chunk(q) + ka);
+            ra[set][q] = load16u(srca.chunk(q) + ka);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            rb[q] = load16u(srcb.chunk(q) + kb);
+            rb[set][q] = load16u(srcb.chunk(q) + kb);
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, int set) {
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[q], q);
+            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[set][q], q);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[q], q);
+            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[set][q], q);
+    };
+    // The same with a set known only at run time (the loop's last slabs).
+    auto stash_any = [&](int buf, int set) {
+        static_for<0, RS>([&](auto i) {
+            if (set == decltype(i)::value) stash(buf, decltype(i)::value);
+        });
     };
     typename OpA::Frag fa[2];
     typename OpB::Frag fb[2];
@@ -840,9 +863,11 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
 
     const int n = n_full;
     if (n > 0) {
-        fetch(0);
-        stash(0);
-        if (n > 1) fetch(1);
+        fetch(0, 0);
+        stash(0, 0);
+#pragma unroll
+        for (int s = 1; s <= RS; ++s)
+            if (n > s) fetch(s, s % RS);
         __syncthreads();
         read_frags(0, g0, 0);
         int t = 0;
@@ -851,18 +876,27 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
         // count the LDS operations in flight and waits for all of them before
         // each slab's first MFMA; straight-line code waits for the fragments
         // only (+2-5% on products of one 64x64 tile per compute unit).
-        //   store slab t+1 (registers) to buffer cur^1, start loading slab
-        //   t+2, multiply this set's groups of slab t but the last;
+        //   store slab t+1 (register set (t+1) % RS) to buffer cur^1, start
+        //   loading slab t+1+RS into that set, multiply this set's groups of
+        //   slab t but the last;
         //   barrier: slab t+1 is complete in LDS, and every wave has finished
         //   reading buffer cur^1's previous contents (slab t-1);
         //   read this set's first group of slab t+1 and multiply the last
         //   group of slab t (the scheduler may lift those MFMAs above the
         //   barrier; pinning them below it with sched_barrier measured 4-8%
         //   slower).
-        for (; t + 2 < n; ++t) {
+        auto steady = [&](int t, auto setc) {
+            constexpr int set = decltype(setc)::value;
             const int cur = t & 1;
-            stash(cur ^ 1);
-            fetch(t + 2);
+            if constexpr (RS > 1) {
+                // Loads complete in order: with at most the newer sets' loads
+                // outstanding, this set's have landed. The compiler's own
+                // count would also wait for the newer sets.
+                static_assert((RS - 1) * (CA + CB) < 16, "the wait count fits its field");
+                __builtin_amdgcn_s_waitcnt(0x0F70 | ((RS - 1) * (CA + CB)));  // vmcnt only
+            }
+            stash(cur ^ 1, set);
+            fetch(t + 1 + RS, set);
 #pragma unroll
             for (int gg = 0; gg + 1 < GW; ++gg) {
                 read_frags(cur, g0 + gg + 1, (gg + 1) & 1);
@@ -873,11 +907,18 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
             read_frags(cur ^ 1, g0, 0);
             mfmas((GW - 1) & 1);
             interleave_b();
-        }
-        // Last two slabs: no more loads.
+        };
+        // RS slabs per pass, so that slab t+1's set, (t+1) % RS, is a
+        // constant in each (t is a multiple of RS at the top of a pass).
+        for (; t + 2 * RS < n; t += RS)
+            static_for<0, RS>([&](auto i) { steady(t + decltype(i)::value, std::integral_constant<int, (decltype(i)::value + 1) % RS>{}); });
+        static_for<0, RS - 1>([&](auto i) {
+            if (t + RS + 1 < n) steady(t++, std::integral_constant<int, (decltype(i)::value + 1) % RS>{});
+        });
+        // Last RS + 1 slabs: no more loads.
         for (; t < n; ++t) {
             const int cur = t & 1;
-            if (t + 1 < n) stash(cur ^ 1);
+            if (t + 1 < n) stash_any(cur ^ 1, (t + 1) % RS);
             multiply_mine(cur);
             __syncthreads();
             if (t + 1 < n) read_frags(cur ^ 1, g0, 0);
@@ -939,7 +980,7 @@ using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE, SGEMM_MFMA_MID_REG_SETS>;
 using MidSplitCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
 using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
 using WideCfg = MfmaConfig<SGEMM_MFMA_WIDE_TILE, SGEMM_MFMA_WIDE_REG_SETS>;
-using KSplitCfg = KSplitConfig<SGEMM_MFMA_KSPLIT_TILE>;
+using KSplitCfg = KSplitConfig<SGEMM_MFMA_KSPLIT_TILE, SGEMM_MFMA_KSPLIT_REG_SETS>;
 
 // Products too small for a single interior tile: general tiles only.
 template <class Cfg, bool TA, bool TB, bool VEC>

@@ -51,6 +51,13 @@
 #ifndef SGEMM_MFMA_KSPLIT_TILE
 #define SGEMM_MFMA_KSPLIT_TILE 64, 64, 32, 2, 2, 2
 #endif
+// Staging register sets of that tile: slab t+1+sets is requested while slab t
+// is multiplied. Two sets against one (interleaved medians on MI355X, TFLOP/s):
+// 1024^3 92.6 -> 97.0, 1024 x 1024 x 4096 109.2 -> 117.5, 1000^3 81.6 -> 86.4,
+// 896^3 72.8 -> 76.0; three and four sets gained less than two.
+#ifndef SGEMM_MFMA_KSPLIT_REG_SETS
+#define SGEMM_MFMA_KSPLIT_REG_SETS 2
+#endif
 
 namespace sgemm_impl {
 
