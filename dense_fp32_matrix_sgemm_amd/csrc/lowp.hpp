@@ -360,14 +360,25 @@ __device__ __forceinline__ void lp_tile(const LpProblem &p, int tm, int tn, shor
         auto partial = [&](auto op, const std::uint16_t *X, std::int64_t ld, std::int64_t f0, std::int64_t extent,
                            short *dst) {
             using Op = decltype(op);
-#pragma unroll 1
-            for (int e = tid; e < Op::kRows * Op::kRowLen; e += NT) {
+            // All of this work-item's loads first, then the LDS stores, so
+            // that the loads are in flight together.
+            constexpr int kPer = Op::kRows * Op::kRowLen / NT;
+            static_assert(kPer * NT == Op::kRows * Op::kRowLen, "whole elements per work-item");
+            short v[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = tid + i * NT;
                 const int r = e / Op::kRowLen, c = e % Op::kRowLen;
                 const int k = Op::KC ? c : r;
                 const std::int64_t f = f0 + (Op::KC ? r : c);
                 const std::int64_t fc = f < extent ? f : extent - 1;
                 const std::int64_t at = Op::KC ? fc * ld + k0 + k : std::int64_t(k0 + k) * ld + fc;
-                dst[r * Op::kPitch + c] = k0 + k < p.K ? short(X[at]) : short(0);
+                v[i] = k0 + k < p.K ? short(X[at]) : short(0);
+            }
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = tid + i * NT;
+                dst[(e / Op::kRowLen) * Op::kPitch + e % Op::kRowLen] = v[i];
             }
         };
         partial(OpA{}, p.A, p.lda, m0, p.M, As[0]);
@@ -707,14 +718,26 @@ __device__ __forceinline__ void lp_dma_tile(const LpProblem &p, int tm, int tn, 
         auto partial = [&](auto op, const std::uint16_t *X, std::int64_t ld, std::int64_t f0, std::int64_t extent,
                            short *dst) {
             using Op = decltype(op);
-#pragma unroll 1
-            for (int e = tid; e < Op::kRows * Op::kRowLen; e += Cfg::kThreads) {
+            // All of this work-item's loads first, then the LDS stores, so
+            // that the loads are in flight together.
+            constexpr int kPer = Op::kRows * Op::kRowLen / Cfg::kThreads;
+            static_assert(kPer * Cfg::kThreads == Op::kRows * Op::kRowLen, "whole elements per work-item");
+            short v[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = tid + i * Cfg::kThreads;
                 const int r = e / Op::kRowLen, c = e % Op::kRowLen;
                 const int k = Op::KC ? c : r;
                 const std::int64_t f = f0 + (Op::KC ? r : c);
                 const std::int64_t fc = f < extent ? f : extent - 1;
                 const std::int64_t at = Op::KC ? fc * ld + k0 + k : std::int64_t(k0 + k) * ld + fc;
-                dst[Op::lds_of(r, c / 8) + c % 8] = k0 + k < p.K ? short(X[at]) : short(0);
+                v[i] = k0 + k < p.K ? short(X[at]) : short(0);
+            }
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = tid + i * Cfg::kThreads;
+                const int r = e / Op::kRowLen, c = e % Op::kRowLen;
+                dst[Op::lds_of(r, c / 8) + c % 8] = v[i];
             }
         };
         partial(OpA{}, p.A, p.lda, m0, p.M, stage_a(0));

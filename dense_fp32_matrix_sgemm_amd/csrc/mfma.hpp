@@ -703,14 +703,31 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
         auto partial = [&](auto op, const float *X, std::int64_t ld, std::int64_t f0, std::int64_t extent,
                            float *dst) {
             using Op = decltype(op);
+            // Batches of this work-item's loads first, then their LDS stores,
+            // so that the loads of a batch are in flight together (the split
+            // schedule's tile body, short of registers, takes one at a time).
+            constexpr int kPer = Op::kRows * Op::kRowLen / NT;
+            static_assert(kPer * NT == Op::kRows * Op::kRowLen, "whole elements per work-item");
+            constexpr int kBatch = RANGE ? 1 : kPer;
+            static_assert(kPer % kBatch == 0, "whole batches");
 #pragma unroll 1
-            for (int e = tid; e < Op::kRows * Op::kRowLen; e += NT) {
-                const int r = e / Op::kRowLen, c = e % Op::kRowLen;
-                const int k = Op::KC ? c : r;
-                const std::int64_t f = f0 + (Op::KC ? r : c);
-                const std::int64_t fc = f < extent ? f : extent - 1;
-                const std::int64_t at = Op::KC ? fc * ld + k0 + k : std::int64_t(k0 + k) * ld + fc;
-                dst[r * Op::kPitch + c] = k0 + k < p.K ? X[at] : 0.0f;
+            for (int i0 = 0; i0 < kPer; i0 += kBatch) {
+                float v[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const int e = tid + (i0 + i) * NT;
+                    const int r = e / Op::kRowLen, c = e % Op::kRowLen;
+                    const int k = Op::KC ? c : r;
+                    const std::int64_t f = f0 + (Op::KC ? r : c);
+                    const std::int64_t fc = f < extent ? f : extent - 1;
+                    const std::int64_t at = Op::KC ? fc * ld + k0 + k : std::int64_t(k0 + k) * ld + fc;
+                    v[i] = k0 + k < p.K ? X[at] : 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const int e = tid + (i0 + i) * NT;
+                    dst[(e / Op::kRowLen) * Op::kPitch + e % Op::kRowLen] = v[i];
+                }
             }
         };
         partial(OpA{}, p.A, p.lda, m0, p.M, As[0]);
@@ -929,14 +946,25 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
         auto partial = [&](auto op, const float *X, std::int64_t ld, std::int64_t f0, std::int64_t extent,
                            float *dst) {
             using Op = decltype(op);
-#pragma unroll 1
-            for (int e = tid; e < Op::kRows * Op::kRowLen; e += NT) {
+            // All of this work-item's loads first, then the LDS stores, so
+            // that the loads are in flight together.
+            constexpr int kPer = Op::kRows * Op::kRowLen / NT;
+            static_assert(kPer * NT == Op::kRows * Op::kRowLen, "whole elements per work-item");
+            float v[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = tid + i * NT;
                 const int r = e / Op::kRowLen, c = e % Op::kRowLen;
                 const int k = Op::KC ? c : r;
                 const std::int64_t f = f0 + (Op::KC ? r : c);
                 const std::int64_t fc = f < extent ? f : extent - 1;
                 const std::int64_t at = Op::KC ? fc * ld + k0 + k : std::int64_t(k0 + k) * ld + fc;
-                dst[r * Op::kPitch + c] = k0 + k < p.K ? X[at] : 0.0f;
+                v[i] = k0 + k < p.K ? X[at] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = tid + i * NT;
+                dst[(e / Op::kRowLen) * Op::kPitch + e % Op::kRowLen] = v[i];
             }
         };
         partial(OpA{}, p.A, p.lda, m0, p.M, As[0]);
