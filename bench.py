@@ -104,15 +104,28 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_launches(call, steps: int, warmup: int):
-    """Warm up, then time `steps` back-to-back launches with one HIP event
-    between consecutive launches on the launch stream. Returns (total ms,
-    list of per-launch ms)."""
+def time_launches(call, steps: int, warmup: int, per_launch: bool = True):
+    """Warm up, then time `steps` back-to-back launches with HIP events on the
+    launch stream. Returns (total ms, list of per-launch ms, or None).
+
+    With per_launch, an event is recorded between consecutive launches, which
+    gives each launch's interval but adds the events' own cost to it (a few
+    microseconds a launch, a tenth of a 1024^3 product). Without, the events
+    bracket the whole run only, so the launches follow each other as a
+    caller's would, and the mean launch time is total / steps."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    if not per_launch:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), None
     events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     events[0].record(stream)
     for i in range(steps):
@@ -283,10 +296,12 @@ def all_configs(lib, sg, dev) -> dict:
             torch.cuda.synchronize()
             one = time.perf_counter() - t0
             reps = int(max(50, min(2000, 0.1 / max(one, 1e-6))))
-            _, per = time_launches(call, reps, 3)
+            tot, _ = time_launches(call, reps, 3, per_launch=False)
+            _, per = time_launches(call, reps, 1)
             med, mn = float(np.median(per)), min(per)
             entry["variants"][name] = {
-                "reps": reps, "ms_median": round(med, 5), "ms_min": round(mn, 5),
+                "reps": reps, "ms_mean_back_to_back": round(tot / reps, 5),
+                "ms_median": round(med, 5), "ms_min": round(mn, 5),
                 "TFLOP/s_median": round(f / (med / 1e3) / 1e12, 3), "TFLOP/s_max": round(f / (mn / 1e3) / 1e12, 3),
                 "frac_of_fp32_peak_median": round(f / (med / 1e3) / 1e12 / PEAK_FP32_TFLOPS, 4),
                 "check_worst_error_over_bound": round(worst, 4)}
@@ -369,13 +384,16 @@ def config_sweep(lib, sg, dev, variant: int) -> dict:
         torch.cuda.synchronize()
         one = time.perf_counter() - t0
         reps = int(max(50, min(2000, 0.2 / max(one, 1e-6))))
-        _, per = time_launches(call, reps, 20)
-        mean, med = sum(per) / len(per), float(np.median(per))
+        # Warm-up long enough (about 50 ms of launches) for the clock to settle.
+        total, _ = time_launches(call, reps, int(max(20, min(4000, 0.05 / max(one, 1e-6)))), per_launch=False)
+        mean = total / reps
+        _, per = time_launches(call, min(reps, 200), 5)
+        med = float(np.median(per))
         f = flops(M, N, K)
         tf = f / (mean / 1e3) / 1e12
         key = f"{M}x{N}x{K}"
         out[key] = {"values": dist, "variant": sg.sgemm_variant_name(resolved), "reps": reps,
-                    "kernel_ms_mean": round(mean, 5), "kernel_ms_median": round(med, 5),
+                    "kernel_ms_mean": round(mean, 5), "kernel_ms_median_with_events_between": round(med, 5),
                     "TFLOP/s": round(tf, 3), "frac": round(tf / PEAK_FP32_TFLOPS, 4),
                     "check_sampled_elements": int(rows.size),
                     "check_worst_error_over_bound": round(float(excess(got, ref, sabs).max()), 4),
@@ -496,7 +514,7 @@ def main(argv=None) -> int:
             torch.cuda.synchronize()
             one = time.perf_counter() - t0
             reps = max(3, min(50, int(0.5 / max(one, 1e-6))))
-            tot, per_v = time_launches(call, reps, 1)
+            tot, _ = time_launches(call, reps, 1, per_launch=False)
             vms = tot / reps
             tf = f / (vms / 1e3) / 1e12
             ladder[name] = {"ms": round(vms, 4), "TFLOP/s": round(tf, 3),
@@ -506,9 +524,9 @@ def main(argv=None) -> int:
 
     log(f"timing {args.steps} steps of variant {sg.sgemm_variant_name(resolved)} "
         f"after {args.warmup} warm-up steps")
-    total_ms, per = time_launches(make_call(variant), args.steps, args.warmup)
+    total_ms, _ = time_launches(make_call(variant), args.steps, args.warmup, per_launch=False)
     ms = total_ms / args.steps
-    kernel_ms = sum(per) / len(per)
+    kernel_ms = ms  # back-to-back launches: the mean launch time
     f = flops(M, N, K)
     value = f / (ms / 1e3) / 1e12
     achieved = f / (kernel_ms / 1e3) / 1e12
@@ -544,7 +562,6 @@ def main(argv=None) -> int:
             "frac": round(achieved / bound_peak, 4),
             "traffic": traffic_per_launch() if (M == 4096 and resolved == sg.SGEMM_MFMA) else None,
             "kernel_ms_mean": round(kernel_ms, 5),
-            "kernel_ms_min": round(min(per), 5),
             "compulsory_bytes": compulsory_bytes(M, N, K),
         },
     }
@@ -598,8 +615,8 @@ def main(argv=None) -> int:
                         call()
                         torch.cuda.synchronize()
                         same = bool(torch.equal(dC2, plain))
-                    tot, per_g = time_launches(call, 50, 10)
-                    kms = sum(per_g) / len(per_g)
+                    tot, _ = time_launches(call, 50, 10, per_launch=False)
+                    kms = tot / 50
                     key = ("t" if ta else "n") + ("t" if tb else "n") + f"_beta{int(beta)}"
                     general[key] = {"kernel_ms_mean": round(kms, 5),
                                     "TFLOP/s": round(f / (kms / 1e3) / 1e12, 3),
@@ -631,8 +648,8 @@ def main(argv=None) -> int:
                                       K if tb else N, 0.0, dC.data_ptr(), N, stream.cuda_stream)
                     if rc != 0:
                         raise sg.SgemmError(rc)
-                tot, per_l = time_launches(call, 50, 10)
-                kms = sum(per_l) / len(per_l)
+                tot, _ = time_launches(call, 50, 10, per_launch=False)
+                kms = tot / 50
                 tf = f / (kms / 1e3) / 1e12
                 torch.cuda.synchronize()
                 Cl = dC.cpu().numpy()
