@@ -26,6 +26,8 @@ Raw entry points (same names and arguments as the C ABI):
     sgemm_variant_name(variant) -> str | None
     sgemm_best_variant(M, N, K) -> variant
     sgemm_mfma_tile(M, N, cus=0) -> (BM, BN)
+    sgemm_mfma_shape(M, N, cus=0) -> (BM, BN, BK, waves M, waves N, k sets)
+    sgemm_regblock_tile(M, N, cus=0) -> tile edge of the REGBLOCK variant
 Pointers are integers (device addresses); ``stream`` is a hipStream_t as an
 integer (0 = null stream).
 
@@ -82,7 +84,7 @@ VARIANTS = {"best": SGEMM_BEST, "naive": SGEMM_NAIVE, "tiled": SGEMM_TILED,
 EXPORTS = ("sgemm", "sgemm_check_args", "sgemm_ex", "sgemm_ex_check_args", "sgemm_ex_ws", "sgemm_ex_ws_check_args",
            "sgemm_ex_workspace_size", "sgemm_ex_noalloc", "sgemm_ex_noalloc_check_args",
            "sgemm_ex_noalloc_scratch_bytes", "sgemm_lp", "sgemm_lp_check_args", "sgemm_status_string", "sgemm_variant_name",
-           "sgemm_best_variant", "sgemm_mfma_tile", "sgemm_mfma_shape")
+           "sgemm_best_variant", "sgemm_mfma_tile", "sgemm_mfma_shape", "sgemm_regblock_tile")
 
 _lib = None
 
@@ -144,6 +146,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_mfma_tile.restype = i
     lib.sgemm_mfma_shape.argtypes = [i, i, i, ip]
     lib.sgemm_mfma_shape.restype = i
+    lib.sgemm_regblock_tile.argtypes = [i, i, i]
+    lib.sgemm_regblock_tile.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -237,6 +241,14 @@ def sgemm_mfma_tile(M: int, N: int, cus: int = 0):
     if rc != SGEMM_OK:
         raise SgemmError(rc)
     return bm.value, bn.value
+
+
+def sgemm_regblock_tile(M: int, N: int, cus: int = 0) -> int:
+    """Edge of the square tile (128, 64 or 32) the REGBLOCK variant uses for M x N."""
+    rc = load_library().sgemm_regblock_tile(M, N, cus)
+    if rc < 0:
+        raise SgemmError(rc)
+    return rc
 
 
 def _variant_code(variant) -> int:

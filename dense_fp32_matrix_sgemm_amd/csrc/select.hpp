@@ -25,6 +25,10 @@ SplitChoice choose_split(int M, int N, int K, int cus);
 // Workspace of the split schedule: two partial tiles per work-group.
 std::size_t split_workspace_bytes(MfmaTile tile, int grid);
 
+// Edge of the square tile (128, 64 or 32) the register-blocked rung takes
+// for an M x N product on `cus` compute units (cus <= 0 means 256).
+int regblock_tile_size(int M, int N, int cus);
+
 // Size of the library's own static scratch buffer (sgemm_ex_noalloc): the
 // largest workspace the split schedule asks for on a 256-CU MI355X (one
 // 256 x 256 work-group per compute unit, two partial tiles each).
