@@ -1001,7 +1001,7 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
 
 // Tile shapes (tiles.hpp).
 using GeneralCfg = MfmaConfig<SGEMM_MFMA_TILE>;
-using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE, SGEMM_MFMA_BIG_REG_SETS>;
+using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
 using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE, SGEMM_MFMA_MID_REG_SETS>;
 // The split schedule runs two 128x128 work-groups per compute unit at once,
 // which needs the one-set register budget.

@@ -27,9 +27,6 @@
 #ifndef SGEMM_MFMA_MID_REG_SETS
 #define SGEMM_MFMA_MID_REG_SETS 2
 #endif
-#ifndef SGEMM_MFMA_BIG_REG_SETS
-#define SGEMM_MFMA_BIG_REG_SETS 1
-#endif
 // 192 x 128 tiles with 2 x 4 waves of 96 x 32, two staging register sets (one
 // work-group per compute unit). Products whose 128 x 128 tiles would leave the
 // compute units unevenly loaded but whose 192 x 128 tiles come out near a
