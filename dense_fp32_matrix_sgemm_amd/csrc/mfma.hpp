@@ -207,6 +207,9 @@ struct OperandRef {
     std::int64_t free_extent;
 };
 
+// How OperandSource::place rotates an FC chunk at the edge (see there).
+enum class Rotate { kSelect, kSelectPinned, kBranch };
+
 // Where one work-item's chunks of an operand tile come from, for the fast
 // tile body: chunk q of every slab starts at chunk(q) + slab offset. With
 // EDGE, addresses are clamped into the operand (see interior_tile) and
@@ -256,15 +259,39 @@ struct OperandSource {
             return base + off[0] + std::int64_t(q) * Op::kRowStep * ld;
     }
     // Element e of chunk q is element e + shift of what was read (the
-    // elements past the operand's edge keep junk).
+    // elements past the operand's edge keep junk). Three forms, chosen per
+    // loop by measurement:
+    //  * kSelect: two steps of one independent select each (by 1, then by
+    //    2), straight-line code. A chain of compares of the shift against 0,
+    //    1 and 2 becomes a switch, compiled to divergent branches that split
+    //    a slab loop's interleaved schedule (the 256 x 256 tile's edge tiles
+    //    ran 4-5% slower with it);
+    //  * kSelectPinned: the same behind an empty asm that ties the rotation
+    //    to the point of the code where the chunk is stored. Free to move in
+    //    a loop with two staging register sets, the selects were computed for
+    //    both sets at the top of the loop, which then waited for the newest
+    //    loads in flight as well;
+    //  * kBranch: the compare chain; its branches skip the rotation in waves
+    //    with no chunk at the edge, which pays in the short slabs of the
+    //    two-set 64 x 64 tile.
+    template <Rotate R>
     __device__ f32x4 place(f32x4 v, int q) const
     {
         if constexpr (EDGE && !Op::KC) {
             const int s = shift[kShifts > 1 ? q : 0];
             f32x4 r;
-            r[0] = s == 0 ? v[0] : s == 1 ? v[1] : s == 2 ? v[2] : v[3];
-            r[1] = s == 0 ? v[1] : s == 1 ? v[2] : v[3];
-            r[2] = s == 0 ? v[2] : v[3];
+            if constexpr (R == Rotate::kBranch) {
+                r[0] = s == 0 ? v[0] : s == 1 ? v[1] : s == 2 ? v[2] : v[3];
+                r[1] = s == 0 ? v[1] : s == 1 ? v[2] : v[3];
+                r[2] = s == 0 ? v[2] : v[3];
+            } else {
+                if constexpr (R == Rotate::kSelectPinned) asm volatile("" : "+v"(v));
+                const bool b0 = (s & 1) != 0, b1 = (s & 2) != 0;
+                const float t0 = b0 ? v[1] : v[0], t1 = b0 ? v[2] : v[1], t2 = b0 ? v[3] : v[2];
+                r[0] = b1 ? t2 : t0;
+                r[1] = b1 ? v[3] : t1;
+                r[2] = b1 ? v[3] : t2;
+            }
             r[3] = v[3];
             return r;
         } else {
@@ -548,6 +575,7 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
     // Slab s is staged in register set s % RS; `set` is always a constant
     // after unrolling, so the sets stay in fixed registers.
     constexpr int RS = Cfg::kRegSets;
+    constexpr Rotate kRot = RS > 1 ? Rotate::kSelectPinned : Rotate::kSelect;
     f32x4 ra[RS][CA], rb[RS][CB];
     auto fetch = [&](int slab, int set) {  // slab counted from s_first
         const std::int64_t ka = (s_first + slab) * slab_a, kb = (s_first + slab) * slab_b;
@@ -561,10 +589,12 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
     auto stash = [&](int buf, int set) {
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[set][q], q);
+            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) =
+                srca.template place<kRot>(ra[set][q], q);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[set][q], q);
+            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) =
+                srcb.template place<kRot>(rb[set][q], q);
     };
 
     typename OpA::Frag fa[2];
@@ -616,8 +646,14 @@ __device__ __forceinline__ void interior_tile(const Problem &p, int tm, int tn, 
     if (n > 0) {
         fetch(0, 0);
         stash(0, 0);
-        if (n > 1) fetch(1, RS - 1);
-        if (RS == 2 && n > 2) fetch(2, 0);
+        // The next slabs' loads are issued whether or not the slabs exist
+        // (slab 0 again in their place, never stored): with the loads under
+        // a branch, the compiler's count of loads in flight at the loop's
+        // head is the one of the path without them, and it then waits for
+        // every load before the last LDS store of each pass, the newer
+        // set's included.
+        fetch(n > 1 ? 1 : 0, RS - 1);
+        if constexpr (RS == 2) fetch(n > 2 ? 2 : 0, 0);
         __syncthreads();
         read_frags(0, 0, 0);
         int t = 0;
@@ -823,10 +859,12 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
     auto stash = [&](int buf, int set) {
 #pragma unroll
         for (int q = 0; q < CA; ++q)
-            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) = srca.place(ra[set][q], q);
+            *reinterpret_cast<f32x4 *>(&As[buf][OpA::chunk_lds(q * NT + tid)]) =
+                srca.template place<Rotate::kBranch>(ra[set][q], q);
 #pragma unroll
         for (int q = 0; q < CB; ++q)
-            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) = srcb.place(rb[set][q], q);
+            *reinterpret_cast<f32x4 *>(&Bs[buf][OpB::chunk_lds(q * NT + tid)]) =
+                srcb.template place<Rotate::kBranch>(rb[set][q], q);
     };
     // The same with a set known only at run time (the loop's last slabs).
     auto stash_any = [&](int buf, int set) {
@@ -882,6 +920,8 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
     if (n > 0) {
         fetch(0, 0);
         stash(0, 0);
+        // Under a branch, unlike interior_tile's: issued unconditionally,
+        // these loads made the tile 1.4% slower at 1024 x 1024 x 4096.
 #pragma unroll
         for (int s = 1; s <= RS; ++s)
             if (n > s) fetch(s, s % RS);
@@ -928,7 +968,9 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
         // RS slabs per pass, so that slab t+1's set, (t+1) % RS, is a
         // constant in each (t is a multiple of RS at the top of a pass).
         for (; t + 2 * RS < n; t += RS)
-            static_for<0, RS>([&](auto i) { steady(t + decltype(i)::value, std::integral_constant<int, (decltype(i)::value + 1) % RS>{}); });
+            static_for<0, RS>([&](auto i) {
+                steady(t + decltype(i)::value, std::integral_constant<int, (decltype(i)::value + 1) % RS>{});
+            });
         static_for<0, RS - 1>([&](auto i) {
             if (t + RS + 1 < n) steady(t++, std::integral_constant<int, (decltype(i)::value + 1) % RS>{});
         });
