@@ -1050,6 +1050,7 @@ using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE, SGEMM_MFMA_MID_REG_SETS>;
 using MidSplitCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
 using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
 using WideCfg = MfmaConfig<SGEMM_MFMA_WIDE_TILE, SGEMM_MFMA_WIDE_REG_SETS>;
+using WideNCfg = MfmaConfig<SGEMM_MFMA_WIDEN_TILE, SGEMM_MFMA_WIDEN_REG_SETS>;
 using KSplitCfg = KSplitConfig<SGEMM_MFMA_KSPLIT_TILE, SGEMM_MFMA_KSPLIT_REG_SETS>;
 
 // Products too small for a single interior tile: general tiles only.
@@ -1249,6 +1250,7 @@ hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
     case MfmaTile::Big: return launch_tiles<BigCfg, TA, TB>(p, stream);
     case MfmaTile::Mid: return launch_tiles<MidCfg, TA, TB>(p, stream);
     case MfmaTile::Wide: return launch_tiles<WideCfg, TA, TB>(p, stream);
+    case MfmaTile::WideN: return launch_tiles<WideNCfg, TA, TB>(p, stream);
     case MfmaTile::KSplit: return launch_ksplit<KSplitCfg, TA, TB>(p, stream);
     case MfmaTile::Small: break;
     }

@@ -55,6 +55,7 @@ const Candidate kCandidates[] = {
     {MfmaTile::Big, tiles::kBig[0], tiles::kBig[1], 1, {1.0, 0, 0, 0}},
     {MfmaTile::Mid, tiles::kMid[0], tiles::kMid[1], 1, {0.91, 0, 0, 0}},
     {MfmaTile::Wide, tiles::kWide[0], tiles::kWide[1], 1, {0.93, 0, 0, 0}},
+    {MfmaTile::WideN, tiles::kWideN[0], tiles::kWideN[1], 1, {0.93, 0, 0, 0}},
     {MfmaTile::Small, tiles::kSmall[0], tiles::kSmall[1], 4, {0.59, 0.72, 0.79, 0.84}},
     {MfmaTile::KSplit, tiles::kKSplit[0], tiles::kKSplit[1], 2, {0.65, 0.78, 0, 0}},
 };
@@ -203,6 +204,7 @@ extern "C" int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN)
     case MfmaTile::Small: dims = tiles::kSmall; break;
     case MfmaTile::KSplit: dims = tiles::kKSplit; break;
     case MfmaTile::Wide: dims = tiles::kWide; break;
+    case MfmaTile::WideN: dims = tiles::kWideN; break;
     }
     *BM = dims[0];
     *BN = dims[1];
@@ -237,6 +239,7 @@ extern "C" int sgemm_mfma_shape(int M, int N, int cus, int *shape)
         sets = tiles::kKSplit[5];
         break;
     case MfmaTile::Wide: dims = tiles::kWide; break;
+    case MfmaTile::WideN: dims = tiles::kWideN; break;
     }
     for (int i = 0; i < 5; ++i) shape[i] = dims[i];
     shape[5] = sets;

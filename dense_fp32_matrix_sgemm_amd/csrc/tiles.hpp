@@ -39,6 +39,16 @@
 #ifndef SGEMM_MFMA_WIDE_REG_SETS
 #define SGEMM_MFMA_WIDE_REG_SETS 2
 #endif
+// The same tile turned round, 128 x 192 with 4 x 2 waves of 32 x 96, for
+// products whose M and N are the other way round: 2047 x 3001 x 4093 takes
+// 16 x 16 of them, one per compute unit, where it took 5.9 64 x 64 tiles per
+// compute unit.
+#ifndef SGEMM_MFMA_WIDEN_TILE
+#define SGEMM_MFMA_WIDEN_TILE 128, 192, 32, 4, 2
+#endif
+#ifndef SGEMM_MFMA_WIDEN_REG_SETS
+#define SGEMM_MFMA_WIDEN_REG_SETS 2
+#endif
 // The small tiles take short slabs: BK = 16 here and 32 below measured 1-3.5%
 // faster than 32 and 64 on every product that uses them, and twice as long
 // lost 5-12%.
@@ -62,7 +72,7 @@
 namespace sgemm_impl {
 
 // Interior tile shape of one matrix-core launch.
-enum class MfmaTile { Big, Mid, Small, KSplit, Wide };
+enum class MfmaTile { Big, Mid, Small, KSplit, Wide, WideN };
 
 namespace tiles {
 constexpr int kGeneral[] = {SGEMM_MFMA_TILE};
@@ -71,6 +81,7 @@ constexpr int kMid[] = {SGEMM_MFMA_MID_TILE};
 constexpr int kSmall[] = {SGEMM_MFMA_SMALL_TILE};
 constexpr int kKSplit[] = {SGEMM_MFMA_KSPLIT_TILE};
 constexpr int kWide[] = {SGEMM_MFMA_WIDE_TILE};
+constexpr int kWideN[] = {SGEMM_MFMA_WIDEN_TILE};
 }  // namespace tiles
 
 }  // namespace sgemm_impl

@@ -224,7 +224,8 @@ def test_mfma_tile_choice(lib):
     assert sg.sgemm_mfma_tile(1024, 1024) == (64, 64)
     assert sg.sgemm_mfma_tile(3001, 2047) == (192, 128)   # 16 x 16 tiles: one per compute unit
     assert sg.sgemm_mfma_tile(3072, 2048) == (192, 128)
-    assert sg.sgemm_mfma_tile(2047, 3001) == (64, 64)
+    assert sg.sgemm_mfma_tile(2047, 3001) == (128, 192)   # the same, turned round
+    assert sg.sgemm_mfma_tile(2048, 3072) == (128, 192)
     assert sg.sgemm_mfma_tile(128, 128) == (64, 64)
     # Fewer compute units shift the choice toward larger tiles.
     assert sg.sgemm_mfma_tile(2048, 2048, cus=64) == (256, 256)
@@ -237,7 +238,7 @@ def test_mfma_shape_choice(lib):
     assert sg.sgemm_mfma_shape(1024, 1024) == (64, 64, 32, 2, 2, 2)
     assert sg.sgemm_mfma_shape(1000, 1000) == (64, 64, 32, 2, 2, 2)
     assert sg.sgemm_mfma_shape(3001, 2047) == (192, 128, 32, 2, 4, 1)
-    assert sg.sgemm_mfma_shape(2047, 3001) == (64, 64, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(2047, 3001) == (128, 192, 32, 4, 2, 1)
     assert sg.sgemm_mfma_shape(4096, 4096) == (256, 256, 16, 4, 2, 1)
     assert sg.sgemm_mfma_shape(2048, 2048) == (128, 128, 32, 2, 4, 1)
     for shape in [(7, 9), (128, 128), (1024, 1024), (3001, 2047), (4096, 4096), (8192, 300)]:
@@ -359,10 +360,12 @@ def test_split_workspace_size(lib):
     # Uneven tile loads take the split schedule: two partial tiles per
     # work-group, one 256x256 work-group per compute unit or two 128x128.
     big, mid = 2 * 256 * 256 * 256 * 4, 2 * 512 * 128 * 128 * 4
-    assert sg.sgemm_ex_workspace_size(N_, N_, 2047, 3001, 4093, 256) == big
+    assert sg.sgemm_ex_workspace_size(N_, N_, 2047, 2560, 4093, 256) == big
     assert sg.sgemm_ex_workspace_size(T_, T_, 3072, 3072, 3072, 0) == big
-    # 3001 x 2047 fits 16 x 16 tiles of 192 x 128, one per compute unit: whole tiles.
+    # 3001 x 2047 fits 16 x 16 tiles of 192 x 128, one per compute unit, and
+    # 2047 x 3001 as many of 128 x 192: whole tiles.
     assert sg.sgemm_ex_workspace_size(N_, N_, 3001, 2047, 4093, 256) == 0
+    assert sg.sgemm_ex_workspace_size(N_, N_, 2047, 3001, 4093, 256) == 0
     assert sg.sgemm_ex_workspace_size(T_, T_, 3072, 2048, 4096, 0) == 0
     assert sg.sgemm_ex_workspace_size(N_, T_, 512, 512, 16384, 256) == mid
     for cus in (64, 128, 304):   # sized for the device's compute units when used
@@ -395,12 +398,12 @@ def test_noalloc_scratch_limit(lib):
     # a device with more would need more for some products, which is a clear
     # error, and only where the matrix-core variant would split.
     limit = sg.sgemm_ex_noalloc_scratch_bytes()
-    assert limit == 128 << 20 == sg.sgemm_ex_workspace_size(N_, N_, 2047, 3001, 4093, 256)
-    ragged = (N_, N_, 2047, 3001, 16384, 1.0, A, 16384, B, 3001, 0.0, C, 3001)
+    assert limit == 128 << 20 == sg.sgemm_ex_workspace_size(N_, N_, 2047, 2560, 4093, 256)
+    ragged = (N_, N_, 2047, 2560, 16384, 1.0, A, 16384, B, 2560, 0.0, C, 2560)
     for cus in (0, 64, 128, 256):
         assert sg.sgemm_ex_noalloc_check_args(*ragged, sg.SGEMM_MFMA, cus) == sg.SGEMM_OK
     for cus in (512, 1024):
-        assert sg.sgemm_ex_workspace_size(N_, N_, 2047, 3001, 16384, cus) > limit
+        assert sg.sgemm_ex_workspace_size(N_, N_, 2047, 2560, 16384, cus) > limit
         assert sg.sgemm_ex_noalloc_check_args(*ragged, sg.SGEMM_MFMA, cus) == sg.SGEMM_ERR_SCRATCH
         assert sg.sgemm_ex_noalloc_check_args(*ragged, sg.SGEMM_BEST, cus) == sg.SGEMM_ERR_SCRATCH
         for v in (sg.SGEMM_NAIVE, sg.SGEMM_TILED, sg.SGEMM_REGBLOCK):   # never split

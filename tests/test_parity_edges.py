@@ -42,8 +42,8 @@ def _stored(x, trans):
 # 1000^3 takes the two-set 64x64 tile (one tile per compute unit), with a
 # partial last slab (1000 = 31 * 32 + 8).
 RAGGED = [((5000, 3000, 333), (256, 256)), ((4300, 4300, 130), (128, 128)), ((3001, 2047, 4093), (192, 128)),
-          ((2047, 3001, 4093), (64, 64)), ((1900, 2100, 77), (128, 128)), ((1000, 1000, 1000), (64, 64)),
-          ((2900, 1910, 515), (192, 128))]
+          ((2047, 3001, 4093), (128, 192)), ((1900, 2100, 77), (128, 128)), ((1000, 1000, 1000), (64, 64)),
+          ((2900, 1910, 515), (192, 128)), ((2040, 3001, 515), (128, 192))]
 KSPLIT = {(1000, 1000, 1000)}
 
 

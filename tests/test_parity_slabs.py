@@ -32,7 +32,7 @@ PAIRS = [(False, False), (False, True), (True, False), (True, True)]
 # around its slab boundaries: 1, under and over one slab, two, three, four,
 # five and six.
 TILES = [((1536, 1500), (64, 64, 16)), ((1000, 1000), (64, 64, 32)), ((3001, 2047), (192, 128, 32)),
-         ((2000, 2040), (128, 128, 32))]
+         ((2047, 3001), (128, 192, 32)), ((2000, 2040), (128, 128, 32))]
 
 
 def _ks(tile):

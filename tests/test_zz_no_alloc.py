@@ -53,7 +53,7 @@ def _run(entry, M, N, K, A, B, C0, alpha, beta, ws=None, tA=False, tB=False):
 # Two calls in a row, the second smaller; both take the split schedule (the
 # first with 256 x 256 pieces, the second with 128 x 128), then a product
 # that keeps whole tiles and needs no scratch.
-SEQUENCE = [(2047, 3001, 4093, False, False), (768, 640, 6000, True, True), (1024, 1024, 1024, False, True)]
+SEQUENCE = [(2047, 2560, 4093, False, False), (768, 640, 6000, True, True), (1024, 1024, 1024, False, True)]
 
 
 def test_scratch_limit_and_plans():
