@@ -13,7 +13,8 @@
 // MI355X with each shape forced over a set of products (TFLOP/s over 256
 // compute units, relative to 147 for 256x256 at 4096^3): 128x128 0.91, one
 // at a time (its two staging register sets leave room for one work-group);
-// 192x128 0.93, one at a time (0.92-0.96 on products it tiles exactly);
+// 192x128 0.93, one at a time (0.92-0.96 on products it tiles exactly),
+// and 128x192, the same tile turned round, likewise;
 // 64x64 0.59, 0.72, 0.79 and 0.84 for one to four;
 // 64x64 with its K range split over two sets of waves 0.65 alone and 0.78 two
 // at a time (it takes 1024^3 from 80 to 95 TFLOP/s). (A 256x128 shape
