@@ -851,6 +851,15 @@ hipError_t lp_launch_tiles(const LpProblem &p, hipStream_t stream)
 #ifndef SGEMM_LP_MID_TILE
 #define SGEMM_LP_MID_TILE 128, 128, 64, 4, 2
 #endif
+// 192 x 128 tiles (2 x 4 waves of 96 x 32) for products whose 128 x 128 tiles
+// would leave the compute units unevenly loaded but whose 192 x 128 tiles take
+// fewer rounds (3001 x 2047 takes 16 x 16 of them, one per compute unit,
+// against 1.5 per compute unit of 128 x 128). With A stored M x K only: the
+// 192-row tile of a transposed A is 24 chunks a row, which the work-items do
+// not split evenly.
+#ifndef SGEMM_LP_WIDE_TILE
+#define SGEMM_LP_WIDE_TILE 192, 128, 64, 2, 4
+#endif
 // The 64x64 tile takes slabs of 64: against 32, +6% at 1024^3 and 1536^3 in
 // an interleaved A/B (the 128x128 tile lost 7-16% with 32 instead of 64).
 #ifndef SGEMM_LP_SMALL_TILE
@@ -862,6 +871,7 @@ hipError_t lp_launch_tiles(const LpProblem &p, hipStream_t stream)
 using LpDmaCfg = LpDmaConfig<SGEMM_LP_DMA_TILE>;
 using LpBigCfg = LpConfig<SGEMM_LP_BIG_TILE>;
 using LpMidCfg = LpConfig<SGEMM_LP_MID_TILE>;
+using LpWideCfg = LpConfig<SGEMM_LP_WIDE_TILE>;
 using LpSmallCfg = LpConfig<SGEMM_LP_SMALL_TILE>;
 
 template <class Cfg>
@@ -884,7 +894,9 @@ bool lp_dma_ok(const LpProblem &p)
 #endif
 }
 
-// The largest tile shape whose tiles give every compute unit at least one.
+// The largest tile shape whose tiles give every compute unit at least one;
+// 192 x 128 instead of 128 x 128 where its rounds of one tile per compute
+// unit cover less area.
 template <LpType T, bool TA, bool TB>
 hipError_t lp_launch(const LpProblem &p, hipStream_t stream)
 {
@@ -899,6 +911,16 @@ hipError_t lp_launch(const LpProblem &p, hipStream_t stream)
     const std::int64_t fill = p.cus > 0 ? p.cus : 256;
     if (lp_tiles<LpDmaCfg>(p) >= fill && lp_dma_ok<TA, TB>(p)) return lp_launch_tiles<LpDmaCfg, T, TA, TB, true>(p, stream);
     if (lp_tiles<LpBigCfg>(p) >= fill) return lp_launch_tiles<LpBigCfg, T, TA, TB>(p, stream);
+    if constexpr (!TA) {
+        // Rounds of one tile per compute unit, times the tile's area.
+        const auto area = [&](std::int64_t tiles, std::int64_t bm, std::int64_t bn) {
+            return (tiles + fill - 1) / fill * bm * bn;
+        };
+        const std::int64_t mid = lp_tiles<LpMidCfg>(p);
+        if (mid >= fill && area(lp_tiles<LpWideCfg>(p), LpWideCfg::BM, LpWideCfg::BN) <
+                               area(mid, LpMidCfg::BM, LpMidCfg::BN))
+            return lp_launch_tiles<LpWideCfg, T, TA, TB>(p, stream);
+    }
     if (lp_tiles<LpMidCfg>(p) >= fill) return lp_launch_tiles<LpMidCfg, T, TA, TB>(p, stream);
     return lp_launch_tiles<LpSmallCfg, T, TA, TB>(p, stream);
 }

@@ -297,3 +297,78 @@ def test_lp_tensor_api():
         C = sg.gemm(dX.t(), dY).cpu().numpy()
         Cref, S = oracle.gemm_ex(True, False, 1.0, X, Y, 0.0, None)
         assert_within(C, Cref, S, f"tensor API {dt}")
+
+
+# The 192 x 128 register-staged tile (A stored M x K: the NN and NT pairs).
+# The launch takes it in place of 128 x 128 where its rounds of one tile per
+# compute unit cover less area: 3001 x 2047 has 16 x 16 of them against
+# 24 x 16 of 128 x 128 (and under 256 of the 256 x 256 tiles).
+def _takes_wide_lp(M, N, tA):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = lambda bm, bn: -(-M // bm) * -(-N // bn)
+    rounds = lambda t: -(-t // cus)
+    return (not tA and tiles(256, 256) < cus and tiles(128, 128) >= cus and
+            rounds(tiles(192, 128)) * 192 * 128 < rounds(tiles(128, 128)) * 128 * 128)
+
+
+WIDE_KS = [1, 16, 63, 64, 65, 129, 192, 255]
+
+
+@pytest.mark.parametrize("pair", [(False, False), (False, True)], ids=["nn", "nt"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_wide_tile_slab_boundaries(dtype, pair):
+    # Small integers over K on both sides of one to four slabs of 64, every
+    # edge partial: the exact integer product over the whole of C.
+    tA, tB = pair
+    M, N = 3001, 2047
+    assert _takes_wide_lp(M, N, tA)
+    for K in WIDE_KS:
+        print(f"[lowp] 192x128 tile {dtype} {M}x{N}x{K} {pair}", flush=True)
+        opA, opB, _ = _case(dtype, M, N, K, K + 50, dist="int")
+        C, _, _ = _run(dtype, tA, tB, 1.0, opA, opB, 0.0, np.zeros((M, N), np.float32))
+        want = opA.astype(np.float64) @ opB.astype(np.float64)
+        assert np.array_equal(C.astype(np.float64), want), (M, N, K, pair)
+
+
+@pytest.mark.parametrize("pair", [(False, False), (False, True)], ids=["nn", "nt"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_lp_wide_tile_padded_window(dtype, pair):
+    # Padded, misaligned operands and C (the register-staged tile reads and
+    # writes at any 2- and 4-byte alignment), alpha and beta, a partial last
+    # slab; sampled against the oracle, and nothing outside C's window changes.
+    tA, tB = pair
+    M, N, K = 2990, 2041, 515
+    assert _takes_wide_lp(M, N, tA)
+    print(f"[lowp] 192x128 tile padded {dtype} {pair}", flush=True)
+    opA, opB, C0 = _case(dtype, M, N, K, 101)
+    A = synth.to_lowp_bits(_stored(opA, tA), dtype)
+    B = synth.to_lowp_bits(_stored(opB, tB), dtype)
+    C, cbuf, ldc, off = gemm_lp(dtype, tA, tB, -1.25, A, B, 0.5, C0, ld_pad=(3, 5, 7), offset=(1, 2, 3),
+                                return_buffer=True)
+    rng = np.random.default_rng(7)
+    rows = np.concatenate([rng.integers(0, M, 3000), np.arange(M - 64, M).repeat(8)])
+    cols = np.concatenate([rng.integers(0, N, 3000), np.arange(N - 64, N).repeat(8)])
+    want, S = oracle.gemm_ex_entries(tA, tB, -1.25, oracle.lowp_to_float32(A, dtype),
+                                     oracle.lowp_to_float32(B, dtype), 0.5, C0, rows, cols)
+    assert_within(C[rows, cols], want, S, f"{dtype} {pair} 192x128 padded")
+    mask = np.ones(cbuf.shape, bool)
+    mask[(off + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]).ravel()] = False
+    assert (cbuf[mask] == SENTINEL).all()
+
+
+@pytest.mark.parametrize("pair", [(False, False), (False, True)], ids=["nn", "nt"])
+def test_lp_wide_tile_same_bits_as_other_tiles(pair):
+    # Every register-staged tile walks k in the same steps of 16 in the same
+    # order, so the top-left 1000 x 1000 of a 192 x 128-tile product equals
+    # the 1000 x 1000 product (64 x 64 tiles) bit for bit.
+    tA, tB = pair
+    M, N, K = 3001, 2047, 777
+    assert _takes_wide_lp(M, N, tA) and not _takes_wide_lp(1000, 1000, tA)
+    print(f"[lowp] 192x128 tile vs 64x64 tile bits {pair}", flush=True)
+    opA, opB, C0 = _case("bf16", M, N, K, 111)
+    full = gemm_lp("bf16", tA, tB, 1.0, synth.to_lowp_bits(_stored(opA, tA), "bf16"),
+                   synth.to_lowp_bits(_stored(opB, tB), "bf16"), 0.0, C0)
+    sub = gemm_lp("bf16", tA, tB, 1.0, synth.to_lowp_bits(_stored(np.ascontiguousarray(opA[:1000]), tA), "bf16"),
+                  synth.to_lowp_bits(_stored(np.ascontiguousarray(opB[:, :1000]), tB), "bf16"), 0.0,
+                  np.ascontiguousarray(C0[:1000, :1000]))
+    assert np.array_equal(full[:1000, :1000].view(np.uint32), sub.view(np.uint32))
