@@ -341,11 +341,36 @@ __device__ __forceinline__ void mfma_group(floatx16 (&acc)[OpA::NB][OpB::NB], co
 // block (a, b) is row OpA::free_index(a, 8(r/4) + 4h + r%4) and column
 // OpB::free_index(b, l32) of the wave tile; the TI blocks of one FC group of
 // B give a lane TI adjacent columns, updated with one access.
+//
+// With beta != 0 the old values of C are read a block (16 rows of TI
+// columns) at a time, all before any of them is written.
 template <class OpA, class OpB>
 __device__ __forceinline__ void write_tile(const Problem &p, const floatx16 (&acc)[OpA::NB][OpB::NB],
                                            std::int64_t r0, int c0, int l32, int h, bool inside)
 {
     constexpr int TB = OpB::TI;
+    if (p.beta != 0.0f) {
+#pragma unroll
+        for (int a = 0; a < OpA::NB; ++a)
+#pragma unroll
+            for (int j = 0; j < OpB::NJ; ++j) {
+                const int col = c0 + j * 32 * TB + l32 * TB;
+                float old[16][TB];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    read_c<TB>(p.C, p.ldc, r0 + OpA::free_index(a, 8 * (r / 4) + 4 * h + (r % 4)), col, p.M, p.N,
+                               inside, old[r]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v[TB];
+#pragma unroll
+                    for (int t = 0; t < TB; ++t) v[t] = acc[a][j * TB + t][r];
+                    write_c<TB>(p.C, p.ldc, r0 + OpA::free_index(a, 8 * (r / 4) + 4 * h + (r % 4)), col, p.M, p.N,
+                                v, old[r], inside, p.alpha, p.beta);
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int a = 0; a < OpA::NB; ++a)
 #pragma unroll

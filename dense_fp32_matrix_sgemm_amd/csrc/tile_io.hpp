@@ -138,6 +138,56 @@ __device__ __forceinline__ void update_n(float *base, std::int64_t ld, std::int6
         if (c + e < cols) p[e] = beta != 0.0f ? axpby(alpha, v[e], beta, p[e]) : alpha * v[e];
 }
 
+// The two halves of update_n for callers that update many runs of C with
+// beta != 0: read_c reads the N elements of a run (0 where a run at the edge
+// has none), write_c writes alpha * v + beta * old over them. Reading every
+// run of a batch before writing any keeps the reads in flight together;
+// update_n, run by run, waits for each read before the next.
+template <int N>
+__device__ __forceinline__ void read_c(const float *base, std::int64_t ld, std::int64_t row, int c, std::int64_t rows,
+                                       int cols, bool inside, float (&old)[N])
+{
+    const float *p = base + row * ld + c;
+    if (inside) {
+        if constexpr (N == 4) {
+            const f32x4u x = load16u(p);
+            old[0] = x[0];
+            old[1] = x[1];
+            old[2] = x[2];
+            old[3] = x[3];
+        } else {
+            __builtin_memcpy(old, p, sizeof(old));
+        }
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < N; ++e) old[e] = row < rows && c + e < cols ? p[e] : 0.0f;
+}
+
+template <int N>
+__device__ __forceinline__ void write_c(float *base, std::int64_t ld, std::int64_t row, int c, std::int64_t rows,
+                                        int cols, const float (&v)[N], const float (&old)[N], bool inside, float alpha,
+                                        float beta)
+{
+    float o[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) o[e] = axpby(alpha, v[e], beta, old[e]);
+    float *p = base + row * ld + c;
+    if (inside) {
+        if constexpr (N == 4)
+            store16u(p, f32x4u{o[0], o[1], o[2], o[3]});
+        else if constexpr (N == 2)
+            store8u(p, o[0], o[1]);
+        else
+            p[0] = o[0];
+        return;
+    }
+    if (row >= rows) return;
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        if (c + e < cols) p[e] = o[e];
+}
+
 // Work-group number -> output tile (tm, tn).
 //
 // The dispatcher hands consecutive work-group numbers to the eight XCDs in
