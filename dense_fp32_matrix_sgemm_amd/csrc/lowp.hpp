@@ -388,17 +388,36 @@ __device__ __forceinline__ void lp_tile(const LpProblem &p, int tm, int tn, shor
     }
 
     // Epilogue: register r of block (a, b) is row 32a + 8(r/4) + 4h + r%4 and
-    // column 32b + l % 32 of the wave tile.
+    // column 32b + l % 32 of the wave tile. With beta != 0 a block's 16 old
+    // values of C are read before any of them is written, so that the reads
+    // are in flight together.
     const int l32 = lane % 32, h = lane / 32;
+    auto row_of = [&](int a, int r) -> std::int64_t { return m0 + wm0 + 32 * a + 8 * (r / 4) + 4 * h + (r % 4); };
+    if (p.beta != 0.0f) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int b = 0; b < NBl; ++b) {
+                const int col = n0 + wn0 + 32 * b + l32;
+                float old[16][1];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) read_c<1>(p.C, p.ldc, row_of(a, r), col, p.M, p.N, !EDGE, old[r]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float v[1] = {acc[a][b][r]};
+                    write_c<1>(p.C, p.ldc, row_of(a, r), col, p.M, p.N, v, old[r], !EDGE, p.alpha, p.beta);
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const std::int64_t row = m0 + wm0 + 32 * a + 8 * (r / 4) + 4 * h + (r % 4);
 #pragma unroll
             for (int b = 0; b < NBl; ++b) {
                 const float v[1] = {acc[a][b][r]};
-                update_n<1>(p.C, p.ldc, row, n0 + wn0 + 32 * b + l32, p.M, p.N, v, !EDGE, p.alpha, p.beta);
+                update_n<1>(p.C, p.ldc, row_of(a, r), n0 + wn0 + 32 * b + l32, p.M, p.N, v, !EDGE, p.alpha, p.beta);
             }
         }
 }
@@ -773,13 +792,25 @@ __device__ __forceinline__ void lp_dma_tile(const LpProblem &p, int tm, int tn, 
                 *reinterpret_cast<f32x4u *>(stage_c + l32 * kPitch + 32 * b + 8 * q + 4 * h) =
                     f32x4u{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's writes before its reads
+        // With beta != 0 the 16 runs' old values of C are read first, so that
+        // the reads are in flight together.
+        float old[16][4];
+        if (p.beta != 0.0f) {
+#pragma unroll
+            for (int it = 0; it < 16; ++it)
+                read_c<4>(p.C, p.ldc, m0 + wm0 + 32 * a + 2 * it + h, n0 + wn0 + 4 * l32, p.M, p.N, inside, old[it]);
+        }
 #pragma unroll
         for (int it = 0; it < 16; ++it) {
             const int row = 2 * it + h;
             const f32x4u x = *reinterpret_cast<const f32x4u *>(stage_c + row * kPitch + 4 * l32);
             const float v[4] = {x[0], x[1], x[2], x[3]};
-            update_n<4>(p.C, p.ldc, m0 + wm0 + 32 * a + row, n0 + wn0 + 4 * l32, p.M, p.N, v, inside, p.alpha,
-                        p.beta);
+            if (p.beta != 0.0f)
+                write_c<4>(p.C, p.ldc, m0 + wm0 + 32 * a + row, n0 + wn0 + 4 * l32, p.M, p.N, v, old[it], inside,
+                           p.alpha, p.beta);
+            else
+                update_n<4>(p.C, p.ldc, m0 + wm0 + 32 * a + row, n0 + wn0 + 4 * l32, p.M, p.N, v, inside, p.alpha,
+                            p.beta);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads before the next block row's writes
     }
