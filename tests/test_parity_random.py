@@ -9,7 +9,8 @@ list names are covered too. Sizes are log-uniform in [1, 3000] (FP32) or
 random entries plus the whole last row and column against the oracle, through
 sgemm_ex (variant best; every third case through sgemm_ex_ws with a workspace)
 for FP32 and through sgemm_lp for bf16 and f16; a third set runs the naive,
-tiled and register-blocked rungs in turn.
+tiled and register-blocked rungs in turn, and a fourth draws large products
+(M and N in [1700, 4400]) for the large tiles of both paths.
 """
 
 import numpy as np
@@ -101,6 +102,59 @@ def test_random_lowp(case):
     opA = synth.lowp_values(3 * i + 101, (M, K), dtype, "pm1")
     opB = synth.lowp_values(3 * i + 102, (K, N), dtype, "pm1")
     C0 = synth.uniform_pm1(3 * i + 103, (M, N))
+    A = synth.to_lowp_bits(_stored(opA, tA), dtype)
+    B = synth.to_lowp_bits(_stored(opB, tB), dtype)
+    C = gemm_lp(dtype, tA, tB, alpha, A, B, beta, C0, ld_pad=pads, offset=offs)
+    rows, cols = _sample(M, N, i)
+    want, S = oracle.gemm_ex_entries(tA, tB, alpha, oracle.lowp_to_float32(A, dtype), oracle.lowp_to_float32(B, dtype),
+                                     beta, C0, rows, cols)
+    assert_within(C[rows, cols], want, S, f"{dtype} {_id(case)}")
+
+
+# Large products: M and N uniform in [1700, 4400], K log-uniform in [1, 3000],
+# so that the large tiles (256 x 256, 192 x 128, 128 x 192, 128 x 128 and the
+# 16-bit ones) run with every edge combination and transpose pair.
+def _large_cases(seed: int, n: int):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M, N = (int(x) for x in rng.integers(1700, 4401, 2))
+        K = max(1, int(np.exp(rng.uniform(0.0, np.log(3000)))))
+        tA, tB = bool(rng.integers(2)), bool(rng.integers(2))
+        alpha, beta = SCALARS[int(rng.integers(len(SCALARS)))]
+        pads = tuple(int(x) for x in rng.integers(0, 6, 3)) if rng.random() < 0.5 else (0, 0, 0)
+        offs = tuple(int(x) for x in rng.integers(0, 4, 3)) if rng.random() < 0.3 else (0, 0, 0)
+        out.append((i, M, N, K, tA, tB, alpha, beta, pads, offs))
+    return out
+
+
+LARGE_CASES = _large_cases(8096, 24)
+
+
+@pytest.mark.parametrize("case", LARGE_CASES, ids=_id)
+def test_random_large_fp32(case, workspace):
+    i, M, N, K, tA, tB, alpha, beta, pads, offs = case
+    print(f"[random] large fp32 {_id(case)} tile {sg.sgemm_mfma_tile(M, N)} alpha {alpha} beta {beta} pads {pads} "
+          f"offsets {offs}", flush=True)
+    opA = synth.uniform_pm1(3 * i + 301, (M, K))
+    opB = synth.uniform_pm1(3 * i + 302, (K, N))
+    C0 = synth.uniform_pm1(3 * i + 303, (M, N))
+    A, B = _stored(opA, tA), _stored(opB, tB)
+    ws = workspace if i % 3 == 0 else None
+    C = gemm_ex(tA, tB, alpha, A, B, beta, C0, "best", ld_pad=pads, offset=offs, workspace=ws)
+    rows, cols = _sample(M, N, i)
+    want, S = oracle.gemm_ex_entries(tA, tB, alpha, A, B, beta, C0, rows, cols)
+    assert_within(C[rows, cols], want, S, _id(case))
+
+
+@pytest.mark.parametrize("case", LARGE_CASES, ids=_id)
+def test_random_large_lowp(case):
+    i, M, N, K, tA, tB, alpha, beta, pads, offs = case
+    dtype = "bf16" if i % 2 == 0 else "f16"
+    print(f"[random] large {dtype} {_id(case)} alpha {alpha} beta {beta} pads {pads} offsets {offs}", flush=True)
+    opA = synth.lowp_values(3 * i + 401, (M, K), dtype, "pm1")
+    opB = synth.lowp_values(3 * i + 402, (K, N), dtype, "pm1")
+    C0 = synth.uniform_pm1(3 * i + 403, (M, N))
     A = synth.to_lowp_bits(_stored(opA, tA), dtype)
     B = synth.to_lowp_bits(_stored(opB, tB), dtype)
     C = gemm_lp(dtype, tA, tB, alpha, A, B, beta, C0, ld_pad=pads, offset=offs)
