@@ -1073,6 +1073,10 @@ using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE, SGEMM_MFMA_MID_REG_SETS>;
 // The split schedule runs two 128x128 work-groups per compute unit at once,
 // which needs the one-set register budget.
 using MidSplitCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
+// Four waves whose 64 accumulator registers a wave and two staging sets fit
+// the budget of two waves per SIMD: two such work-groups per compute unit.
+using MidDualCfg = MfmaConfig<SGEMM_MFMA_MID_DUAL_TILE, SGEMM_MFMA_MID_DUAL_REG_SETS>;
+static_assert(MidDualCfg::kWavesPerEU * 4 == 2 * MidDualCfg::kThreads / 64, "two work-groups per compute unit");
 using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
 using WideCfg = MfmaConfig<SGEMM_MFMA_WIDE_TILE, SGEMM_MFMA_WIDE_REG_SETS>;
 using WideNCfg = MfmaConfig<SGEMM_MFMA_WIDEN_TILE, SGEMM_MFMA_WIDEN_REG_SETS>;
@@ -1274,6 +1278,7 @@ hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
     switch (p.tile) {
     case MfmaTile::Big: return launch_tiles<BigCfg, TA, TB>(p, stream);
     case MfmaTile::Mid: return launch_tiles<MidCfg, TA, TB>(p, stream);
+    case MfmaTile::MidDual: return launch_tiles<MidDualCfg, TA, TB>(p, stream);
     case MfmaTile::Wide: return launch_tiles<WideCfg, TA, TB>(p, stream);
     case MfmaTile::WideN: return launch_tiles<WideNCfg, TA, TB>(p, stream);
     case MfmaTile::KSplit: return launch_ksplit<KSplitCfg, TA, TB>(p, stream);

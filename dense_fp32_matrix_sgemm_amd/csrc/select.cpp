@@ -13,6 +13,9 @@
 // MI355X with each shape forced over a set of products (TFLOP/s over 256
 // compute units, relative to 147 for 256x256 at 4096^3): 128x128 0.91, one
 // at a time (its two staging register sets leave room for one work-group);
+// 128x128 in four waves 0.89 alone and 0.925 two at a time (two such
+// work-groups share a compute unit; 2-3% ahead of the eight-wave 128x128
+// tile wherever a compute unit holds two or more, level or behind with one);
 // 192x128 0.93, one at a time (0.92-0.96 on products it tiles exactly),
 // and 128x192, the same tile turned round, likewise;
 // 64x64 0.59, 0.72, 0.79 and 0.84 for one to four;
@@ -55,6 +58,7 @@ double launch_time(const Candidate &c, std::int64_t M, std::int64_t N, std::int6
 const Candidate kCandidates[] = {
     {MfmaTile::Big, tiles::kBig[0], tiles::kBig[1], 1, {1.0, 0, 0, 0}},
     {MfmaTile::Mid, tiles::kMid[0], tiles::kMid[1], 1, {0.91, 0, 0, 0}},
+    {MfmaTile::MidDual, tiles::kMidDual[0], tiles::kMidDual[1], 2, {0.89, 0.925, 0, 0}},
     {MfmaTile::Wide, tiles::kWide[0], tiles::kWide[1], 1, {0.93, 0, 0, 0}},
     {MfmaTile::WideN, tiles::kWideN[0], tiles::kWideN[1], 1, {0.93, 0, 0, 0}},
     {MfmaTile::Small, tiles::kSmall[0], tiles::kSmall[1], 4, {0.59, 0.72, 0.79, 0.84}},
@@ -206,6 +210,7 @@ extern "C" int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN)
     case MfmaTile::KSplit: dims = tiles::kKSplit; break;
     case MfmaTile::Wide: dims = tiles::kWide; break;
     case MfmaTile::WideN: dims = tiles::kWideN; break;
+    case MfmaTile::MidDual: dims = tiles::kMidDual; break;
     }
     *BM = dims[0];
     *BN = dims[1];
@@ -241,6 +246,7 @@ extern "C" int sgemm_mfma_shape(int M, int N, int cus, int *shape)
         break;
     case MfmaTile::Wide: dims = tiles::kWide; break;
     case MfmaTile::WideN: dims = tiles::kWideN; break;
+    case MfmaTile::MidDual: dims = tiles::kMidDual; break;
     }
     for (int i = 0; i < 5; ++i) shape[i] = dims[i];
     shape[5] = sets;

@@ -11,7 +11,8 @@
 #endif
 // Tiles of the fast loop, largest first. The 256x256 and 128x128 tiles run eight
 // waves (two per SIMD), so one wave's loads, LDS traffic and barrier waits
-// overlap the other's matrix instructions; the 64x64 tile runs four.
+// overlap the other's matrix instructions; the 64x64 tile runs four, and so
+// does the second 128x128 tile, of which two work-groups share a compute unit.
 #ifndef SGEMM_MFMA_BIG_TILE
 #define SGEMM_MFMA_BIG_TILE 256, 256, 16, 4, 2
 #endif
@@ -26,6 +27,20 @@
 // (four work-groups per compute unit) loses with one.
 #ifndef SGEMM_MFMA_MID_REG_SETS
 #define SGEMM_MFMA_MID_REG_SETS 2
+#endif
+// 128 x 128 tiles with 2 x 2 waves of 64 x 64, slabs of 16 and two staging
+// register sets: four waves and 36 KB of LDS, so two work-groups share a
+// compute unit, and one's loads, stores and barrier waits overlap the other's
+// matrix instructions. Where a compute unit holds two or more 128 x 128
+// tiles this beat the eight-wave tile above by 2-3% (interleaved medians on
+// MI355X, TFLOP/s: 6144^3 143.4 -> 145.9, 4096 x 2048 x 4096 140.1 -> 143.3,
+// 2048 x 4096 x 2048 136.9 -> 140.9); with one tile per compute unit it was
+// level or up to 1.5% slower (2048^3), and slabs of 32 lost 7-9%.
+#ifndef SGEMM_MFMA_MID_DUAL_TILE
+#define SGEMM_MFMA_MID_DUAL_TILE 128, 128, 16, 2, 2
+#endif
+#ifndef SGEMM_MFMA_MID_DUAL_REG_SETS
+#define SGEMM_MFMA_MID_DUAL_REG_SETS 2
 #endif
 // 192 x 128 tiles with 2 x 4 waves of 96 x 32, two staging register sets (one
 // work-group per compute unit). Products whose 128 x 128 tiles would leave the
@@ -72,7 +87,7 @@
 namespace sgemm_impl {
 
 // Interior tile shape of one matrix-core launch.
-enum class MfmaTile { Big, Mid, Small, KSplit, Wide, WideN };
+enum class MfmaTile { Big, Mid, Small, KSplit, Wide, WideN, MidDual };
 
 namespace tiles {
 constexpr int kGeneral[] = {SGEMM_MFMA_TILE};
@@ -82,6 +97,7 @@ constexpr int kSmall[] = {SGEMM_MFMA_SMALL_TILE};
 constexpr int kKSplit[] = {SGEMM_MFMA_KSPLIT_TILE};
 constexpr int kWide[] = {SGEMM_MFMA_WIDE_TILE};
 constexpr int kWideN[] = {SGEMM_MFMA_WIDEN_TILE};
+constexpr int kMidDual[] = {SGEMM_MFMA_MID_DUAL_TILE};
 }  // namespace tiles
 
 }  // namespace sgemm_impl

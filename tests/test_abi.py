@@ -241,7 +241,13 @@ def test_mfma_shape_choice(lib):
     assert sg.sgemm_mfma_shape(2047, 3001) == (128, 192, 32, 4, 2, 1)
     assert sg.sgemm_mfma_shape(4096, 4096) == (256, 256, 16, 4, 2, 1)
     assert sg.sgemm_mfma_shape(2048, 2048) == (128, 128, 32, 2, 4, 1)
-    for shape in [(7, 9), (128, 128), (1024, 1024), (3001, 2047), (4096, 4096), (8192, 300)]:
+    # Two or more 128 x 128 tiles per compute unit: the four-wave tile, two
+    # work-groups to a compute unit; one per compute unit: the eight-wave one.
+    assert sg.sgemm_mfma_shape(2048, 4096) == (128, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(4000, 5000) == (128, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(16384, 512) == (128, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(8192, 512) == (128, 128, 32, 2, 4, 1)
+    for shape in [(7, 9), (128, 128), (1024, 1024), (3001, 2047), (4096, 4096), (8192, 300), (2048, 4096)]:
         assert sg.sgemm_mfma_shape(*shape)[:2] == sg.sgemm_mfma_tile(*shape)
     shp = (ctypes.c_int * 6)()
     assert lib.sgemm_mfma_shape(-1, 4, 0, shp) == sg.SGEMM_ERR_DIM

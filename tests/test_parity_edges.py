@@ -4,7 +4,8 @@ Tiles that cross the bottom or right edge of C run the same loop as the
 others, with their reads clamped into the operands and the partial chunk of
 a row-contiguous operand read from a shifted address and rotated into place.
 These tests run ragged products whose chosen tile shape (each of 256x256,
-192x128, 128x128, 64x64 and the 64x64 tile whose slabs two wave sets share) leaves
+192x128, 128x192, both 128x128 tiles, 64x64 and the 64x64 tile whose slabs
+two wave sets share) leaves
 partial tiles on both edges, for every transpose pair, with alpha and beta,
 and the narrowest widths the clamped reads allow (4 to 7) next to the general
 path below them. Every comparison is with the
@@ -38,12 +39,13 @@ def _stored(x, trans):
     return np.ascontiguousarray(x.T) if trans else x
 
 
-# (M, N, K) and the tile shape the library picks for it (checked on the host);
-# 1000^3 takes the two-set 64x64 tile (one tile per compute unit), with a
-# partial last slab (1000 = 31 * 32 + 8).
-RAGGED = [((5000, 3000, 333), (256, 256)), ((4300, 4300, 130), (128, 128)), ((3001, 2047, 4093), (192, 128)),
-          ((2047, 3001, 4093), (128, 192)), ((1900, 2100, 77), (128, 128)), ((1000, 1000, 1000), (64, 64)),
-          ((2900, 1910, 515), (192, 128)), ((2040, 3001, 515), (128, 192))]
+# (M, N, K) and the tile shape (BM, BN, BK) the library picks for it (checked
+# on the host); 1000^3 takes the two-set 64x64 tile (one tile per compute
+# unit), with a partial last slab (1000 = 31 * 32 + 8); 4300^2 and 2001 x 4095
+# hold two or more 128x128 tiles per compute unit and take the four-wave one.
+RAGGED = [((5000, 3000, 333), (256, 256, 16)), ((4300, 4300, 130), (128, 128, 16)), ((3001, 2047, 4093), (192, 128, 32)),
+          ((2047, 3001, 4093), (128, 192, 32)), ((1900, 2100, 77), (128, 128, 32)), ((1000, 1000, 1000), (64, 64, 32)),
+          ((2900, 1910, 515), (192, 128, 32)), ((2040, 3001, 515), (128, 192, 32)), ((2001, 4095, 1001), (128, 128, 16))]
 KSPLIT = {(1000, 1000, 1000)}
 
 
@@ -52,7 +54,7 @@ KSPLIT = {(1000, 1000, 1000)}
 def test_edge_tiles_of_every_shape(shape, tile, pair):
     M, N, K = shape
     tA, tB = pair
-    assert sg.sgemm_mfma_tile(M, N) == tile
+    assert sg.sgemm_mfma_shape(M, N)[:3] == tile
     assert (sg.sgemm_mfma_shape(M, N)[5] == 2) == (shape in KSPLIT)
     print(f"[edges] {M}x{N}x{K} tile {tile} pair {pair}", flush=True)
     opA = synth.uniform_pm1(M + 11, (M, K))

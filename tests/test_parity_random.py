@@ -112,8 +112,9 @@ def test_random_lowp(case):
 
 
 # Large products: M and N uniform in [1700, 4400], K log-uniform in [1, 3000],
-# so that the large tiles (256 x 256, 192 x 128, 128 x 192, 128 x 128 and the
-# 16-bit ones) run with every edge combination and transpose pair.
+# so that the large tiles (256 x 256, 192 x 128, 128 x 192, both 128 x 128
+# tiles and the 16-bit ones) run with every edge combination and transpose
+# pair.
 def _large_cases(seed: int, n: int):
     rng = np.random.default_rng(seed)
     out = []

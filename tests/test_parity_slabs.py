@@ -3,7 +3,8 @@
 The plain 64x64 tile walks K in slabs of 16 and the two-set tile in slabs of
 32, whose two halves the two wave sets share; the 192x128 and 128x128 tiles
 walk slabs of 32 staged through two register sets, two slabs per pass of
-their unrolled loop. A product runs its whole slabs through the pipelined
+their unrolled loop, and the four-wave 128x128 tile (two work-groups to a
+compute unit) slabs of 16 the same way. A product runs its whole slabs through the pipelined
 loop (the steady state needs three or more, the last ones run without loads)
 and the partial last slab, if any, separately. These tests
 take K on both sides of every such boundary, up to three whole slabs plus a
@@ -32,7 +33,7 @@ PAIRS = [(False, False), (False, True), (True, False), (True, True)]
 # around its slab boundaries: 1, under and over one slab, two, three, four,
 # five and six.
 TILES = [((1536, 1500), (64, 64, 16)), ((1000, 1000), (64, 64, 32)), ((3001, 2047), (192, 128, 32)),
-         ((2047, 3001), (128, 192, 32)), ((2000, 2040), (128, 128, 32))]
+         ((2047, 3001), (128, 192, 32)), ((2000, 2040), (128, 128, 32)), ((2040, 4001), (128, 128, 16))]
 
 
 def _ks(tile):
