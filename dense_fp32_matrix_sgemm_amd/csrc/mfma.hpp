@@ -1070,13 +1070,16 @@ __device__ __forceinline__ void ksplit_tile(const Problem &p, int tm, int tn, fl
 using GeneralCfg = MfmaConfig<SGEMM_MFMA_TILE>;
 using BigCfg = MfmaConfig<SGEMM_MFMA_BIG_TILE>;
 using MidCfg = MfmaConfig<SGEMM_MFMA_MID_TILE, SGEMM_MFMA_MID_REG_SETS>;
-// The split schedule runs two 128x128 work-groups per compute unit at once,
-// which needs the one-set register budget.
-using MidSplitCfg = MfmaConfig<SGEMM_MFMA_MID_TILE>;
 // Four waves whose 64 accumulator registers a wave and two staging sets fit
 // the budget of two waves per SIMD: two such work-groups per compute unit.
 using MidDualCfg = MfmaConfig<SGEMM_MFMA_MID_DUAL_TILE, SGEMM_MFMA_MID_DUAL_REG_SETS>;
 static_assert(MidDualCfg::kWavesPerEU * 4 == 2 * MidDualCfg::kThreads / 64, "two work-groups per compute unit");
+// The split schedule's 128x128 pieces run two work-groups per compute unit
+// too: the four-wave tile, with one staging set (two measured the same). They
+// ran 4-6% faster than eight-wave pieces with one set (interleaved medians on
+// MI355X, TFLOP/s: 1536^3 95.2 -> 100.6, 512 x 512 x 16384 103.2 -> 107.7,
+// 768 x 768 x 8192 108.0 -> 112.5).
+using MidSplitCfg = MfmaConfig<SGEMM_MFMA_MID_DUAL_TILE>;
 using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
 using WideCfg = MfmaConfig<SGEMM_MFMA_WIDE_TILE, SGEMM_MFMA_WIDE_REG_SETS>;
 using WideNCfg = MfmaConfig<SGEMM_MFMA_WIDEN_TILE, SGEMM_MFMA_WIDEN_REG_SETS>;
@@ -1263,7 +1266,7 @@ hipError_t launch_sk(const Problem &p, float *ws, int grid, hipStream_t stream)
 template <bool TA, bool TB>
 hipError_t launch_sk_by_tile(const Problem &p, MfmaTile tile, float *ws, int grid, hipStream_t stream)
 {
-    if (tile == MfmaTile::Mid) return launch_sk<MidSplitCfg, TA, TB>(p, ws, grid, stream);
+    if (tile == MfmaTile::MidDual) return launch_sk<MidSplitCfg, TA, TB>(p, ws, grid, stream);
     return launch_sk<BigCfg, TA, TB>(p, ws, grid, stream);
 }
 

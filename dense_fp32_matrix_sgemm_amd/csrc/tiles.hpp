@@ -22,9 +22,8 @@
 // The 128x128 tile of whole-tile launches stages two slabs in registers
 // (loads issued two slabs before they are stored to LDS; +3-5% at 2048^3),
 // which takes the register budget of one work-group per compute unit. The
-// split schedule's 128x128 pieces keep one set (two work-groups per compute
-// unit), the 256x256 tile has no room for a second set, and the 64x64 tile
-// (four work-groups per compute unit) loses with one.
+// 256x256 tile has no room for a second set, and the 64x64 tile (four
+// work-groups per compute unit) loses with one.
 #ifndef SGEMM_MFMA_MID_REG_SETS
 #define SGEMM_MFMA_MID_REG_SETS 2
 #endif
@@ -35,7 +34,8 @@
 // tiles this beat the eight-wave tile above by 2-3% (interleaved medians on
 // MI355X, TFLOP/s: 6144^3 143.4 -> 145.9, 4096 x 2048 x 4096 140.1 -> 143.3,
 // 2048 x 4096 x 2048 136.9 -> 140.9); with one tile per compute unit it was
-// level or up to 1.5% slower (2048^3), and slabs of 32 lost 7-9%.
+// level or up to 1.5% slower (2048^3), and slabs of 32 lost 7-9%. The split
+// schedule's 128x128 pieces are this tile with one staging set.
 #ifndef SGEMM_MFMA_MID_DUAL_TILE
 #define SGEMM_MFMA_MID_DUAL_TILE 128, 128, 16, 2, 2
 #endif
