@@ -42,24 +42,29 @@
 #ifndef SGEMM_MFMA_MID_DUAL_REG_SETS
 #define SGEMM_MFMA_MID_DUAL_REG_SETS 2
 #endif
-// 192 x 128 tiles with 2 x 4 waves of 96 x 32, two staging register sets (one
-// work-group per compute unit). Products whose 128 x 128 tiles would leave the
-// compute units unevenly loaded but whose 192 x 128 tiles come out near a
-// whole number per compute unit take them: 3001 x 2047 x 4093 (16 x 16 tiles)
-// went from 116 to 132 TFLOP/s against the 64 x 64 tile, 3072 x 2048 x 4096
-// from 126 to 142 (interleaved medians on MI355X).
+// 192 x 128 tiles with 2 x 2 waves of 96 x 64, slabs of 16 and two staging
+// register sets (47 KB of LDS; two work-groups fit a compute unit). Products
+// whose 128 x 128 tiles would leave the compute units unevenly loaded but
+// whose 192 x 128 tiles come out near a whole number per compute unit take
+// them: 3001 x 2047 x 4093 (16 x 16 tiles) went from 116 to 132 TFLOP/s
+// against the 64 x 64 tile, 3072 x 2048 x 4096 from 126 to 142 (interleaved
+// medians on MI355X), with 2 x 4 waves of 96 x 32 and slabs of 32. The four
+// waves then gained 1-3% where a compute unit holds one such tile (3001 x
+// 2047 x 4093 135.3 -> 136.9, 3072 x 2048 x 4096 141.5 -> 143.6) and 3% where
+// it holds several (6144^3 143.7 -> 148.1).
 #ifndef SGEMM_MFMA_WIDE_TILE
-#define SGEMM_MFMA_WIDE_TILE 192, 128, 32, 2, 4
+#define SGEMM_MFMA_WIDE_TILE 192, 128, 16, 2, 2
 #endif
 #ifndef SGEMM_MFMA_WIDE_REG_SETS
 #define SGEMM_MFMA_WIDE_REG_SETS 2
 #endif
-// The same tile turned round, 128 x 192 with 4 x 2 waves of 32 x 96, for
+// The same tile turned round, 128 x 192 with 2 x 2 waves of 64 x 96, for
 // products whose M and N are the other way round: 2047 x 3001 x 4093 takes
 // 16 x 16 of them, one per compute unit, where it took 5.9 64 x 64 tiles per
-// compute unit.
+// compute unit (four waves against eight of 32 x 96: 129.4 -> 133.5 TFLOP/s,
+// 2048 x 3072 x 4096 137.9 -> 142.1).
 #ifndef SGEMM_MFMA_WIDEN_TILE
-#define SGEMM_MFMA_WIDEN_TILE 128, 192, 32, 4, 2
+#define SGEMM_MFMA_WIDEN_TILE 128, 192, 16, 2, 2
 #endif
 #ifndef SGEMM_MFMA_WIDEN_REG_SETS
 #define SGEMM_MFMA_WIDEN_REG_SETS 2

@@ -237,8 +237,8 @@ def test_mfma_shape_choice(lib):
     # waves per SIMD); several resident per compute unit, the plain one.
     assert sg.sgemm_mfma_shape(1024, 1024) == (64, 64, 32, 2, 2, 2)
     assert sg.sgemm_mfma_shape(1000, 1000) == (64, 64, 32, 2, 2, 2)
-    assert sg.sgemm_mfma_shape(3001, 2047) == (192, 128, 32, 2, 4, 1)
-    assert sg.sgemm_mfma_shape(2047, 3001) == (128, 192, 32, 4, 2, 1)
+    assert sg.sgemm_mfma_shape(3001, 2047) == (192, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(2047, 3001) == (128, 192, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(4096, 4096) == (256, 256, 16, 4, 2, 1)
     assert sg.sgemm_mfma_shape(2048, 2048) == (128, 128, 32, 2, 4, 1)
     # Two or more 128 x 128 tiles per compute unit: the four-wave tile, two

@@ -43,9 +43,9 @@ def _stored(x, trans):
 # on the host); 1000^3 takes the two-set 64x64 tile (one tile per compute
 # unit), with a partial last slab (1000 = 31 * 32 + 8); 4300^2 and 2001 x 4095
 # hold two or more 128x128 tiles per compute unit and take the four-wave one.
-RAGGED = [((5000, 3000, 333), (256, 256, 16)), ((4300, 4300, 130), (128, 128, 16)), ((3001, 2047, 4093), (192, 128, 32)),
-          ((2047, 3001, 4093), (128, 192, 32)), ((1900, 2100, 77), (128, 128, 32)), ((1000, 1000, 1000), (64, 64, 32)),
-          ((2900, 1910, 515), (192, 128, 32)), ((2040, 3001, 515), (128, 192, 32)), ((2001, 4095, 1001), (128, 128, 16))]
+RAGGED = [((5000, 3000, 333), (256, 256, 16)), ((4300, 4300, 130), (128, 128, 16)), ((3001, 2047, 4093), (192, 128, 16)),
+          ((2047, 3001, 4093), (128, 192, 16)), ((1900, 2100, 77), (128, 128, 32)), ((1000, 1000, 1000), (64, 64, 32)),
+          ((2900, 1910, 515), (192, 128, 16)), ((2040, 3001, 515), (128, 192, 16)), ((2001, 4095, 1001), (128, 128, 16))]
 KSPLIT = {(1000, 1000, 1000)}
 
 

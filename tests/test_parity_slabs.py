@@ -1,12 +1,12 @@
 """Slab boundaries of the matrix-core tiles (GPU tests).
 
 The plain 64x64 tile walks K in slabs of 16 and the two-set tile in slabs of
-32, whose two halves the two wave sets share; the 192x128 and 128x128 tiles
-walk slabs of 32 staged through two register sets, two slabs per pass of
-their unrolled loop, and the four-wave 128x128 tile (two work-groups to a
-compute unit) slabs of 16 the same way. A product runs its whole slabs through the pipelined
-loop (the steady state needs three or more, the last ones run without loads)
-and the partial last slab, if any, separately. These tests
+32, whose two halves the two wave sets share; the eight-wave 128x128 tile
+walks slabs of 32 staged through two register sets, two slabs per pass of its
+unrolled loop, and the four-wave 192x128, 128x192 and 128x128 tiles slabs of
+16 the same way. A product runs its whole slabs through the pipelined loop
+(the steady state needs three or more, the last ones run without loads) and
+the partial last slab, if any, separately. These tests
 take K on both sides of every such boundary, up to three whole slabs plus a
 partial one, for every transpose pair:
 - small-integer operands, where every partial sum is exact and the whole of C
@@ -32,8 +32,8 @@ PAIRS = [(False, False), (False, True), (True, False), (True, True)]
 # (M, N), the tile (BM, BN, BK) the library picks for it, and the K values
 # around its slab boundaries: 1, under and over one slab, two, three, four,
 # five and six.
-TILES = [((1536, 1500), (64, 64, 16)), ((1000, 1000), (64, 64, 32)), ((3001, 2047), (192, 128, 32)),
-         ((2047, 3001), (128, 192, 32)), ((2000, 2040), (128, 128, 32)), ((2040, 4001), (128, 128, 16))]
+TILES = [((1536, 1500), (64, 64, 16)), ((1000, 1000), (64, 64, 32)), ((3001, 2047), (192, 128, 16)),
+         ((2047, 3001), (128, 192, 16)), ((2000, 2040), (128, 128, 32)), ((2040, 4001), (128, 128, 16))]
 
 
 def _ks(tile):
