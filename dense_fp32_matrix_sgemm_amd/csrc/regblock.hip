@@ -9,8 +9,9 @@
 // 128 x 128 with 8 x 8 per work-item: per k it reads 8 values of A and 8 of B
 // from LDS with four 16-byte reads and does 64 multiply-adds, where the tiled
 // rung did 1 multiply-add per 2 LDS reads. Products with too few of those
-// tiles to occupy the chip take 64 x 64 tiles (4 x 4 per work-item) or
-// 32 x 32 tiles (2 x 2), with the same loop.
+// tiles to occupy the chip take 64 x 64 tiles (4 x 4 per work-item), 32 x 32
+// tiles (2 x 2) or, for the smallest, 16 x 16 tiles (1 x 1, slabs of 64),
+// with the same loop.
 //
 // Layout and scheduling:
 //  * the work-item (tx, ty) of a 16 x 16 grid owns rows VM*ty .. VM*ty+VM-1
@@ -56,6 +57,10 @@ struct RbConfig {
 template <int V>
 struct RbVec;
 template <>
+struct RbVec<1> {
+    typedef float type;
+};
+template <>
 struct RbVec<4> {
     typedef float4 type;
 };
@@ -73,9 +78,11 @@ __device__ __forceinline__ void rb_read(float *dst, const float *src)
         dst[1] = v.y;
         dst[2] = v.z;
         dst[3] = v.w;
-    } else {
+    } else if constexpr (V == 2) {
         dst[0] = v.x;
         dst[1] = v.y;
+    } else {
+        dst[0] = v;
     }
 }
 
@@ -190,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void regblock_kernel(Problem p, int tiles
 using RbLarge = RbConfig<128, 128, 8>;  // the pages' tile: 8 x 8 per work-item
 using RbMid = RbConfig<64, 64, 16>;     // 4 x 4
 using RbSmall = RbConfig<32, 32, 32>;   // 2 x 2
+using RbTiny = RbConfig<16, 16, 64>;    // 1 x 1
 
 template <class Cfg, bool TA, bool TB>
 hipError_t launch(const Problem &p, hipStream_t stream)
@@ -214,6 +222,7 @@ hipError_t launch_cfg(const Problem &p, hipStream_t stream)
 hipError_t launch_regblock(const Problem &p, hipStream_t stream)
 {
     switch (regblock_tile_size(p.M, p.N, p.cus)) {
+    case 16: return launch_cfg<RbTiny>(p, stream);
     case 32: return launch_cfg<RbSmall>(p, stream);
     case 64: return launch_cfg<RbMid>(p, stream);
     default: return launch_cfg<RbLarge>(p, stream);

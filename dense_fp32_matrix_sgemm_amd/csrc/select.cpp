@@ -169,13 +169,15 @@ SplitChoice choose_split(int M, int N, int K, int cus)
 
 // The register-blocked rung's tile: the pages' 128 x 128 where C holds at
 // least one and a half of them per compute unit, else 64 x 64 where it holds
-// at least one per two compute units, else 32 x 32. Measured on MI355X with
+// at least one per two compute units, else 32 x 32 where it holds at least
+// one of those per two compute units, else 16 x 16. Measured on MI355X with
 // each tile forced (back-to-back launches, microseconds, 128 / 64 / 32):
 // 512^3 91 / 32 / 18; 1024^3 198 / 67 / 87; 1536^3 301 / 228 / 251; 2048^3
 // 398 / 301 / 567; 3001 x 2047 x 4093 905 / 963 / 1684; 4096^3 1669 / 2179 /
 // 4370. One 128 x 128 tile per compute unit (2048^3) leaves one wave per SIMD
 // with nothing to hide its latencies behind, so there the 64 x 64 tile's four
-// per compute unit win.
+// per compute unit win. 32 / 16: 128^3 6.0 / 3.9; 256^3 9.9 / 5.7; 300 x 257
+// x 513 19.7 / 15.3; 384^3 14.3 / 14.5; 512^3 18.3 / 23.6.
 int regblock_tile_size(int M, int N, int cus)
 {
 #if defined(SGEMM_REGBLOCK_FORCE_TILE)
@@ -188,7 +190,8 @@ int regblock_tile_size(int M, int N, int cus)
     auto tiles = [&](int t) { return ceil_div(M, t) * ceil_div(N, t); };
     if (2 * tiles(128) >= 3 * n_cus) return 128;
     if (2 * tiles(64) >= n_cus) return 64;
-    return 32;
+    if (2 * tiles(32) >= n_cus) return 32;
+    return 16;
 #endif
 }
 

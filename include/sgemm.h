@@ -77,8 +77,9 @@ typedef enum sgemm_op {
  *  REGBLOCK 128 x 128 LDS tiles, an 8 x 8 block of C per work-item in
  *           registers, 128-bit global loads, double-buffered LDS (same page,
  *           section 07; "From 306 ms to 86 ms", "Register blocking"); 64 x 64
- *           (4 x 4) or 32 x 32 (2 x 2) tiles for products with too few
- *           128 x 128 tiles to occupy the device (sgemm_regblock_tile).
+ *           (4 x 4), 32 x 32 (2 x 2) or 16 x 16 (1 x 1) tiles for products
+ *           with too few 128 x 128 tiles to occupy the device
+ *           (sgemm_regblock_tile).
  *  MFMA     the same tiling fed to the CDNA matrix cores with
  *           v_mfma_f32_32x32x2_f32 (FP32 in, FP32 accumulate), with the tile
  *           shape chosen per product (sgemm_mfma_tile, sgemm_mfma_shape).
@@ -350,7 +351,7 @@ const char *sgemm_variant_name(int variant);
 int sgemm_best_variant(int M, int N, int K);
 
 /*
- * Edge of the square tile (128, 64 or 32) the REGBLOCK variant uses for an
+ * Edge of the square tile (128, 64, 32 or 16) the REGBLOCK variant uses for an
  * M x N product on a device with `cus` compute units (cus <= 0: 256, an
  * MI355X): the pages' 128 x 128 tile ("From 306 ms to 86 ms", "Register
  * blocking") where C holds enough of them to occupy the compute units, else

@@ -263,8 +263,8 @@ def test_mfma_tile_errors(lib):
 
 def test_regblock_tile_choice(lib):
     # The pages' 128 x 128 tile where C holds at least 1.5 of them per compute
-    # unit, 64 x 64 where it holds at least one per two compute units, else
-    # 32 x 32.
+    # unit, 64 x 64 where it holds at least one per two compute units, 32 x 32
+    # where it holds at least one of those per two compute units, else 16 x 16.
     assert sg.sgemm_regblock_tile(4096, 4096) == 128
     assert sg.sgemm_regblock_tile(3001, 2047) == 128     # 24 x 16 = 384 tiles: exactly 1.5 per CU
     assert sg.sgemm_regblock_tile(3001, 1919) == 64      # 24 x 15 = 360
@@ -273,9 +273,12 @@ def test_regblock_tile_choice(lib):
     assert sg.sgemm_regblock_tile(768, 768) == 64        # 12 x 12 = 144 tiles of 64
     assert sg.sgemm_regblock_tile(768, 640) == 32        # 12 x 10 = 120 < 128
     assert sg.sgemm_regblock_tile(512, 512) == 32        # 64 tiles of 64
-    assert sg.sgemm_regblock_tile(128, 128) == 32
-    assert sg.sgemm_regblock_tile(1, 1) == 32
-    assert sg.sgemm_regblock_tile(0, 0) == 32
+    assert sg.sgemm_regblock_tile(384, 384) == 32        # 12 x 12 = 144 tiles of 32
+    assert sg.sgemm_regblock_tile(384, 320) == 16        # 12 x 10 = 120 < 128
+    assert sg.sgemm_regblock_tile(256, 256) == 16        # 64 tiles of 32
+    assert sg.sgemm_regblock_tile(128, 128) == 16
+    assert sg.sgemm_regblock_tile(1, 1) == 16
+    assert sg.sgemm_regblock_tile(0, 0) == 16
     assert sg.sgemm_regblock_tile(2048, 2048, cus=64) == 128
     assert sg.sgemm_regblock_tile(4096, 4096, cus=0) == sg.sgemm_regblock_tile(4096, 4096, cus=256)
     assert lib.sgemm_regblock_tile(-1, 4, 0) == sg.SGEMM_ERR_DIM

@@ -2,9 +2,9 @@
 
 The rung keeps a block of C per work-item in registers ("From 306 ms to 86
 ms", "Register blocking"; "Matrix Multiplication -- Naive to Tiled", section
-07): the pages' 128 x 128 tile with 8 x 8 per work-item, and 64 x 64 (4 x 4)
-or 32 x 32 (2 x 2) tiles for products with too few of those to occupy the
-device. sgemm_regblock_tile names the tile a shape takes; every case below
+07): the pages' 128 x 128 tile with 8 x 8 per work-item, and 64 x 64 (4 x 4),
+32 x 32 (2 x 2) or 16 x 16 (1 x 1) tiles for products with too few of those
+to occupy the device. sgemm_regblock_tile names the tile a shape takes; every case below
 first checks that its shape takes the tile it is meant to cover. Each tile
 must give the oracle's result within the acceptance bound, the exact integer
 product on small integers, and never write outside C's window. Every
@@ -43,16 +43,18 @@ def _takes(M, N, tile):
     assert sg.sgemm_regblock_tile(M, N, cus) == tile, (M, N, tile)
 
 
-# Shapes per tile (slab depth BK = 8, 16, 32): a whole number of tiles, and
-# each side one past and one short of a tile edge, with K around the slab.
+# Shapes per tile (slab depth BK = 8, 16, 32, 64): a whole number of tiles,
+# and each side one past and one short of a tile edge, with K around the slab.
 EDGES = {
     128: [(3072, 2048, 64), (3073, 2047, 65), (3071, 2049, 63), (4095, 1921, 7)],
     64: [(1024, 1024, 64), (1025, 1023, 17), (1023, 1025, 15), (960, 1087, 1)],
-    32: [(32, 32, 32), (33, 31, 33), (31, 33, 31), (1, 1, 1), (2, 3, 5), (1, 300, 129), (300, 1, 129), (65, 33, 7)],
+    32: [(384, 384, 32), (385, 383, 33), (383, 385, 31), (420, 390, 7)],
+    16: [(16, 16, 64), (17, 15, 65), (15, 17, 63), (1, 1, 1), (2, 3, 5), (1, 300, 129), (300, 1, 129), (65, 33, 7),
+         (128, 128, 128)],
 }
 
 
-@pytest.mark.parametrize("tile", [128, 64, 32])
+@pytest.mark.parametrize("tile", [128, 64, 32, 16])
 def test_tile_edges_and_window(tile):
     for (M, N, K) in EDGES[tile]:
         _takes(M, N, tile)
@@ -67,7 +69,8 @@ def test_tile_edges_and_window(tile):
         assert (buf[mask] == SENTINEL).all(), f"regblock {M}x{N}x{K} wrote outside C"
 
 
-@pytest.mark.parametrize("tile,shape", [(128, (3001, 2047, 4093)), (64, (1000, 1000, 1000)), (32, (300, 257, 513))])
+@pytest.mark.parametrize("tile,shape", [(128, (3001, 2047, 4093)), (64, (1000, 1000, 1000)), (32, (400, 400, 513)),
+                                        (16, (300, 257, 513))])
 def test_small_integers_bit_exact(tile, shape):
     M, N, K = shape
     _takes(M, N, tile)
@@ -77,7 +80,8 @@ def test_small_integers_bit_exact(tile, shape):
     assert np.array_equal(gemm(A, B, "regblock").astype(np.float64), oracle.gemm(A, B))
 
 
-@pytest.mark.parametrize("tile,shape", [(128, (3001, 2047, 65)), (64, (1000, 700, 301)), (32, (203, 170, 301))])
+@pytest.mark.parametrize("tile,shape", [(128, (3001, 2047, 65)), (64, (1000, 700, 301)), (32, (420, 390, 301)),
+                                        (16, (203, 170, 301))])
 def test_general_form_every_pair(tile, shape):
     M, N, K = shape
     _takes(M, N, tile)
@@ -101,14 +105,16 @@ def test_general_form_every_pair(tile, shape):
 def test_tiles_sum_alike():
     # The same rows and columns from products that take different tiles: the
     # top-left 1000 x 1000 corner of 3001 x 2047 (128 x 128 tiles) equals the
-    # 1000 x 1000 product (64 x 64) and its 300 x 257 corner (32 x 32) bit for
-    # bit, as every tile sums each element in the same order.
+    # 1000 x 1000 product (64 x 64), its 400 x 400 corner (32 x 32) and that
+    # one's 300 x 257 corner (16 x 16) bit for bit, as every tile sums each
+    # element in the same order.
     K = 777
     A, B = synth.operands(3001, 2047, K, "pm1", seed_a=31, seed_b=32)
     outs = {}
-    for tile, (M, N) in [(128, (3001, 2047)), (64, (1000, 1000)), (32, (300, 257))]:
+    for tile, (M, N) in [(128, (3001, 2047)), (64, (1000, 1000)), (32, (400, 400)), (16, (300, 257))]:
         _takes(M, N, tile)
         _announce(f"tile {tile}: {M}x{N}x{K}")
         outs[tile] = gemm(np.ascontiguousarray(A[:M]), np.ascontiguousarray(B[:, :N]), "regblock")
     assert np.array_equal(outs[128][:1000, :1000], outs[64])
-    assert np.array_equal(outs[64][:300, :257], outs[32])
+    assert np.array_equal(outs[64][:400, :400], outs[32])
+    assert np.array_equal(outs[32][:300, :257], outs[16])
