@@ -1084,6 +1084,7 @@ using SmallCfg = MfmaConfig<SGEMM_MFMA_SMALL_TILE>;
 using WideCfg = MfmaConfig<SGEMM_MFMA_WIDE_TILE, SGEMM_MFMA_WIDE_REG_SETS>;
 using WideNCfg = MfmaConfig<SGEMM_MFMA_WIDEN_TILE, SGEMM_MFMA_WIDEN_REG_SETS>;
 using KSplitCfg = KSplitConfig<SGEMM_MFMA_KSPLIT_TILE, SGEMM_MFMA_KSPLIT_REG_SETS>;
+using KSplit32Cfg = KSplitConfig<SGEMM_MFMA_KSPLIT32_TILE, SGEMM_MFMA_KSPLIT_REG_SETS>;
 
 // Products too small for a single interior tile: general tiles only.
 template <class Cfg, bool TA, bool TB, bool VEC>
@@ -1285,6 +1286,7 @@ hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
     case MfmaTile::Wide: return launch_tiles<WideCfg, TA, TB>(p, stream);
     case MfmaTile::WideN: return launch_tiles<WideNCfg, TA, TB>(p, stream);
     case MfmaTile::KSplit: return launch_ksplit<KSplitCfg, TA, TB>(p, stream);
+    case MfmaTile::KSplit32: return launch_ksplit<KSplit32Cfg, TA, TB>(p, stream);
     case MfmaTile::Small: break;
     }
     return launch_tiles<SmallCfg, TA, TB>(p, stream);

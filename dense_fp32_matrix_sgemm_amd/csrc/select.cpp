@@ -20,7 +20,12 @@
 // and 128x192, the same tile turned round, likewise;
 // 64x64 0.59, 0.72, 0.79 and 0.84 for one to four;
 // 64x64 with its K range split over two sets of waves 0.65 alone and 0.78 two
-// at a time (it takes 1024^3 from 80 to 95 TFLOP/s). (A 256x128 shape
+// at a time (it takes 1024^3 from 80 to 95 TFLOP/s); 32x32 split the same way
+// over two single waves 0.25, 0.30, 0.40 and 0.50 for one to four (fitted so
+// that it takes the products that give each compute unit at most one such
+// tile: 128^3 to 512^3, 300 x 257 x 513 and 512 x 512 x 4096 ran 17-63%
+// faster on it; with two per compute unit 700^3 and 1000 x 300 x 1000 ran
+// 8-10% slower, and 768^3 and 1024^3 3-8% slower). (A 256x128 shape
 // measured 0.85-0.94 alone and never beat these.) The 64x64 rates predate
 // those tiles' shorter slabs, which made both 2-4% faster; with the kernels
 // as they are, a forced-shape run of 14 products found this choice within 1%
@@ -63,6 +68,7 @@ const Candidate kCandidates[] = {
     {MfmaTile::WideN, tiles::kWideN[0], tiles::kWideN[1], 1, {0.93, 0, 0, 0}},
     {MfmaTile::Small, tiles::kSmall[0], tiles::kSmall[1], 4, {0.59, 0.72, 0.79, 0.84}},
     {MfmaTile::KSplit, tiles::kKSplit[0], tiles::kKSplit[1], 2, {0.65, 0.78, 0, 0}},
+    {MfmaTile::KSplit32, tiles::kKSplit32[0], tiles::kKSplit32[1], 4, {0.25, 0.30, 0.40, 0.50}},
 };
 
 }  // namespace
@@ -217,6 +223,7 @@ extern "C" int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN)
     case MfmaTile::Wide: dims = tiles::kWide; break;
     case MfmaTile::WideN: dims = tiles::kWideN; break;
     case MfmaTile::MidDual: dims = tiles::kMidDual; break;
+    case MfmaTile::KSplit32: dims = tiles::kKSplit32; break;
     }
     *BM = dims[0];
     *BN = dims[1];
@@ -249,6 +256,10 @@ extern "C" int sgemm_mfma_shape(int M, int N, int cus, int *shape)
     case MfmaTile::KSplit:
         dims = tiles::kKSplit;
         sets = tiles::kKSplit[5];
+        break;
+    case MfmaTile::KSplit32:
+        dims = tiles::kKSplit32;
+        sets = tiles::kKSplit32[5];
         break;
     case MfmaTile::Wide: dims = tiles::kWide; break;
     case MfmaTile::WideN: dims = tiles::kWideN; break;

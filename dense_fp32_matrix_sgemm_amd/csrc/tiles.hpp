@@ -88,11 +88,20 @@
 #ifndef SGEMM_MFMA_KSPLIT_REG_SETS
 #define SGEMM_MFMA_KSPLIT_REG_SETS 2
 #endif
+// The same split over two sets of one wave each on 32 x 32 tiles, for the
+// smallest products, which leave most compute units without a 64 x 64 tile
+// (interleaved medians on MI355X, microseconds, 64 x 64 -> 32 x 32: 128^3
+// 5.4 -> 4.5, 256^3 7.6 -> 5.7, 384^3 9.5 -> 6.4, 512^3 11.8 -> 7.9,
+// 512 x 512 x 4096 70.1 -> 43.0; 768^3 16.7 -> 17.3 and 1024^3 22.3 -> 24.2
+// stay on the 64 x 64 tiles).
+#ifndef SGEMM_MFMA_KSPLIT32_TILE
+#define SGEMM_MFMA_KSPLIT32_TILE 32, 32, 32, 1, 1, 2
+#endif
 
 namespace sgemm_impl {
 
 // Interior tile shape of one matrix-core launch.
-enum class MfmaTile { Big, Mid, Small, KSplit, Wide, WideN, MidDual };
+enum class MfmaTile { Big, Mid, Small, KSplit, Wide, WideN, MidDual, KSplit32 };
 
 namespace tiles {
 constexpr int kGeneral[] = {SGEMM_MFMA_TILE};
@@ -103,6 +112,7 @@ constexpr int kKSplit[] = {SGEMM_MFMA_KSPLIT_TILE};
 constexpr int kWide[] = {SGEMM_MFMA_WIDE_TILE};
 constexpr int kWideN[] = {SGEMM_MFMA_WIDEN_TILE};
 constexpr int kMidDual[] = {SGEMM_MFMA_MID_DUAL_TILE};
+constexpr int kKSplit32[] = {SGEMM_MFMA_KSPLIT32_TILE};
 }  // namespace tiles
 
 }  // namespace sgemm_impl

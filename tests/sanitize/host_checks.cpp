@@ -92,7 +92,7 @@ int main()
                 const int rt = sgemm_mfma_tile(M, N, cus, &bm, &bn);
                 expect(is_status(rt), "sgemm_mfma_tile status", M, N, cus);
                 if (rt == SGEMM_OK)
-                    expect(((bm == 64 || bm == 128 || bm == 256) && bn == bm) || (bm == 192 && bn == 128) ||
+                    expect(((bm == 32 || bm == 64 || bm == 128 || bm == 256) && bn == bm) || (bm == 192 && bn == 128) ||
                                (bm == 128 && bn == 192),
                            "tile", M, N, bm);
                 int shape[6] = {-1, -1, -1, -1, -1, -1};

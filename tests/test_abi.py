@@ -226,7 +226,9 @@ def test_mfma_tile_choice(lib):
     assert sg.sgemm_mfma_tile(3072, 2048) == (192, 128)
     assert sg.sgemm_mfma_tile(2047, 3001) == (128, 192)   # the same, turned round
     assert sg.sgemm_mfma_tile(2048, 3072) == (128, 192)
-    assert sg.sgemm_mfma_tile(128, 128) == (64, 64)
+    assert sg.sgemm_mfma_tile(128, 128) == (32, 32)     # at most one 32 x 32 tile per compute unit
+    assert sg.sgemm_mfma_tile(512, 512) == (32, 32)
+    assert sg.sgemm_mfma_tile(640, 640) == (64, 64)     # two 32 x 32 tiles per compute unit
     # Fewer compute units shift the choice toward larger tiles.
     assert sg.sgemm_mfma_tile(2048, 2048, cus=64) == (256, 256)
     assert sg.sgemm_mfma_tile(4096, 4096, cus=0) == sg.sgemm_mfma_tile(4096, 4096, cus=256)
@@ -237,6 +239,8 @@ def test_mfma_shape_choice(lib):
     # waves per SIMD); several resident per compute unit, the plain one.
     assert sg.sgemm_mfma_shape(1024, 1024) == (64, 64, 32, 2, 2, 2)
     assert sg.sgemm_mfma_shape(1000, 1000) == (64, 64, 32, 2, 2, 2)
+    assert sg.sgemm_mfma_shape(128, 128) == (32, 32, 32, 1, 1, 2)
+    assert sg.sgemm_mfma_shape(300, 257) == (32, 32, 32, 1, 1, 2)
     assert sg.sgemm_mfma_shape(3001, 2047) == (192, 128, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(2047, 3001) == (128, 192, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(4096, 4096) == (256, 256, 16, 4, 2, 1)

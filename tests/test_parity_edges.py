@@ -4,8 +4,8 @@ Tiles that cross the bottom or right edge of C run the same loop as the
 others, with their reads clamped into the operands and the partial chunk of
 a row-contiguous operand read from a shifted address and rotated into place.
 These tests run ragged products whose chosen tile shape (each of 256x256,
-192x128, 128x192, both 128x128 tiles, 64x64 and the 64x64 tile whose slabs
-two wave sets share) leaves
+192x128, 128x192, both 128x128 tiles, 64x64, and the 64x64 and 32x32 tiles
+whose slabs two wave sets share) leaves
 partial tiles on both edges, for every transpose pair, with alpha and beta,
 and the narrowest widths the clamped reads allow (4 to 7) next to the general
 path below them. Every comparison is with the
@@ -42,11 +42,13 @@ def _stored(x, trans):
 # (M, N, K) and the tile shape (BM, BN, BK) the library picks for it (checked
 # on the host); 1000^3 takes the two-set 64x64 tile (one tile per compute
 # unit), with a partial last slab (1000 = 31 * 32 + 8); 4300^2 and 2001 x 4095
-# hold two or more 128x128 tiles per compute unit and take the four-wave one.
+# hold two or more 128x128 tiles per compute unit and take the four-wave one;
+# 300 x 257 and 37 x 45 take the 32x32 tile whose slabs two single waves share.
 RAGGED = [((5000, 3000, 333), (256, 256, 16)), ((4300, 4300, 130), (128, 128, 16)), ((3001, 2047, 4093), (192, 128, 16)),
           ((2047, 3001, 4093), (128, 192, 16)), ((1900, 2100, 77), (128, 128, 32)), ((1000, 1000, 1000), (64, 64, 32)),
-          ((2900, 1910, 515), (192, 128, 16)), ((2040, 3001, 515), (128, 192, 16)), ((2001, 4095, 1001), (128, 128, 16))]
-KSPLIT = {(1000, 1000, 1000)}
+          ((2900, 1910, 515), (192, 128, 16)), ((2040, 3001, 515), (128, 192, 16)), ((2001, 4095, 1001), (128, 128, 16)),
+          ((300, 257, 513), (32, 32, 32)), ((37, 45, 77), (32, 32, 32))]
+KSPLIT = {(1000, 1000, 1000), (300, 257, 513), (37, 45, 77)}
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)

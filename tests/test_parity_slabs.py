@@ -1,7 +1,7 @@
 """Slab boundaries of the matrix-core tiles (GPU tests).
 
-The plain 64x64 tile walks K in slabs of 16 and the two-set tile in slabs of
-32, whose two halves the two wave sets share; the eight-wave 128x128 tile
+The plain 64x64 tile walks K in slabs of 16 and the two-set 64x64 and 32x32
+tiles in slabs of 32, whose two halves the two wave sets share; the eight-wave 128x128 tile
 walks slabs of 32 staged through two register sets, two slabs per pass of its
 unrolled loop, and the four-wave 192x128, 128x192 and 128x128 tiles slabs of
 16 the same way. A product runs its whole slabs through the pipelined loop
@@ -33,7 +33,8 @@ PAIRS = [(False, False), (False, True), (True, False), (True, True)]
 # around its slab boundaries: 1, under and over one slab, two, three, four,
 # five and six.
 TILES = [((1536, 1500), (64, 64, 16)), ((1000, 1000), (64, 64, 32)), ((3001, 2047), (192, 128, 16)),
-         ((2047, 3001), (128, 192, 16)), ((2000, 2040), (128, 128, 32)), ((2040, 4001), (128, 128, 16))]
+         ((2047, 3001), (128, 192, 16)), ((2000, 2040), (128, 128, 32)), ((2040, 4001), (128, 128, 16)),
+         ((300, 257), (32, 32, 32))]
 
 
 def _ks(tile):
