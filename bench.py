@@ -399,7 +399,7 @@ def config_sweep(lib, sg, dev, variant: int) -> dict:
                     "check_worst_error_over_bound": round(float(excess(got, ref, sabs).max()), 4),
                     "check_pass": bool(within(got, ref, sabs).all())}
         if resolved == sg.SGEMM_MFMA:
-            out[key]["mfma_tile"] = "x".join(str(v) for v in sg.sgemm_mfma_shape(M, N)[:3])
+            out[key]["mfma_tile"] = "x".join(str(v) for v in sg.sgemm_mfma_shape(M, N, K)[:3])
         log(f"config {key}: {mean:.4f} ms mean, {tf:.2f} TFLOP/s, check {out[key]['check_worst_error_over_bound']}")
         del dA, dB, dC
     return out

@@ -25,8 +25,8 @@ Raw entry points (same names and arguments as the C ABI):
     sgemm_status_string(status) -> str
     sgemm_variant_name(variant) -> str | None
     sgemm_best_variant(M, N, K) -> variant
-    sgemm_mfma_tile(M, N, cus=0) -> (BM, BN)
-    sgemm_mfma_shape(M, N, cus=0) -> (BM, BN, BK, waves M, waves N, k sets)
+    sgemm_mfma_tile(M, N, K, cus=0) -> (BM, BN)
+    sgemm_mfma_shape(M, N, K, cus=0) -> (BM, BN, BK, waves M, waves N, k sets)
     sgemm_regblock_tile(M, N, cus=0) -> tile edge of the REGBLOCK variant
 Pointers are integers (device addresses); ``stream`` is a hipStream_t as an
 integer (0 = null stream).
@@ -142,9 +142,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sgemm_best_variant.argtypes = [i, i, i]
     lib.sgemm_best_variant.restype = i
     ip = ctypes.POINTER(ctypes.c_int)
-    lib.sgemm_mfma_tile.argtypes = [i, i, i, ip, ip]
+    lib.sgemm_mfma_tile.argtypes = [i, i, i, i, ip, ip]
     lib.sgemm_mfma_tile.restype = i
-    lib.sgemm_mfma_shape.argtypes = [i, i, i, ip]
+    lib.sgemm_mfma_shape.argtypes = [i, i, i, i, ip]
     lib.sgemm_mfma_shape.restype = i
     lib.sgemm_regblock_tile.argtypes = [i, i, i]
     lib.sgemm_regblock_tile.restype = i
@@ -225,19 +225,19 @@ def sgemm_best_variant(M: int, N: int, K: int) -> int:
     return load_library().sgemm_best_variant(M, N, K)
 
 
-def sgemm_mfma_shape(M: int, N: int, cus: int = 0):
-    """(BM, BN, BK, waves along M, waves along N, k sets) of the MFMA kernel for an M x N product."""
+def sgemm_mfma_shape(M: int, N: int, K: int, cus: int = 0):
+    """(BM, BN, BK, waves along M, waves along N, k sets) of the MFMA kernel for an M x N x K product."""
     shape = (ctypes.c_int * 6)()
-    rc = load_library().sgemm_mfma_shape(M, N, cus, shape)
+    rc = load_library().sgemm_mfma_shape(M, N, K, cus, shape)
     if rc != SGEMM_OK:
         raise SgemmError(rc)
     return tuple(shape)
 
 
-def sgemm_mfma_tile(M: int, N: int, cus: int = 0):
-    """(BM, BN) of the interior tile the MFMA variant uses for M x N."""
+def sgemm_mfma_tile(M: int, N: int, K: int, cus: int = 0):
+    """(BM, BN) of the interior tile the MFMA variant uses for M x N x K."""
     bm, bn = ctypes.c_int(), ctypes.c_int()
-    rc = load_library().sgemm_mfma_tile(M, N, cus, ctypes.byref(bm), ctypes.byref(bn))
+    rc = load_library().sgemm_mfma_tile(M, N, K, cus, ctypes.byref(bm), ctypes.byref(bn))
     if rc != SGEMM_OK:
         raise SgemmError(rc)
     return bm.value, bn.value

@@ -98,7 +98,7 @@ extern "C" int sgemm_ex(int transA, int transB, int M, int N, int K, float alpha
     if (cus == 0) return SGEMM_ERR_DEVICE;
 
     const sgemm_impl::Problem p{A,     B,    C,   lda, ldb, ldc, M, N, K, cus, transA == SGEMM_OP_T, transB == SGEMM_OP_T,
-                                alpha, beta, sgemm_impl::choose_mfma_tile(M, N, cus)};
+                                alpha, beta, sgemm_impl::choose_mfma_tile(M, N, K, cus)};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (variant == SGEMM_BEST) variant = sgemm_best_variant(M, N, K);
 

@@ -51,6 +51,7 @@
 
 #include "gemm.hpp"
 #include "tile_io.hpp"
+#include "wsplit.hpp"
 
 namespace sgemm_impl {
 namespace {
@@ -94,9 +95,6 @@ struct MfmaConfig {
     static constexpr int kRegSets = REG_SETS_;
     static_assert(kRegSets == 1 || kRegSets == 2, "one or two staging register sets");
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-#ifndef SGEMM_MFMA_GROUP_M
-#define SGEMM_MFMA_GROUP_M 8
-#endif
     static constexpr int kGroupM = SGEMM_MFMA_GROUP_M;
     // Waves per SIMD the register allocation aims at: one when a wave's
     // accumulators alone fill the 256 AGPRs, more as they shrink.
@@ -1287,6 +1285,11 @@ hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
     case MfmaTile::WideN: return launch_tiles<WideNCfg, TA, TB>(p, stream);
     case MfmaTile::KSplit: return launch_ksplit<KSplitCfg, TA, TB>(p, stream);
     case MfmaTile::KSplit32: return launch_ksplit<KSplit32Cfg, TA, TB>(p, stream);
+    case MfmaTile::WSplit:
+        // Buffer offsets are formed in 31 bits; larger operands take the
+        // two-set 64 x 64 tile.
+        if (wsplit_offsets_fit(p)) return launch_wsplit<TA, TB>(p, stream);
+        return launch_ksplit<KSplitCfg, TA, TB>(p, stream);
     case MfmaTile::Small: break;
     }
     return launch_tiles<SmallCfg, TA, TB>(p, stream);

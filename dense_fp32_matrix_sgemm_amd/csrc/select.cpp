@@ -29,7 +29,15 @@
 // measured 0.85-0.94 alone and never beat these.) The 64x64 rates predate
 // those tiles' shorter slabs, which made both 2-4% faster; with the kernels
 // as they are, a forced-shape run of 14 products found this choice within 1%
-// of the fastest shape on every one.
+// of the fastest shape on every one. The 64x64 tile whose K range is split
+// over its four waves (wsplit.hpp) runs at 0.75 alone (1024^3: 111 TFLOP/s)
+// and 0.82 two at a time (2048 x 1024 x 1024: 121), ahead of the two-set
+// tile wherever either would be chosen (interleaved medians on MI355X,
+// TFLOP/s, two-set -> four-wave split: 1024^3 102.6 -> 111.2, 1000^3 89.9 ->
+// 94.4, 768^3 54.9 -> 58.6, 2048 x 1024 x 1024 116.0 -> 121.0, 1536^3 90.3
+// -> 95.9); it loses where it gives most compute units no tile at all
+// (512 x 512 x 4096: 49.4 on the 32x32 tile, 31.9 on it), and where a compute
+// unit holds three or more (2048^3: 116 against 135 for 128x128).
 //
 // Pure C++ (no HIP), so it is tested on the host.
 #include <cstddef>
@@ -69,16 +77,45 @@ const Candidate kCandidates[] = {
     {MfmaTile::Small, tiles::kSmall[0], tiles::kSmall[1], 4, {0.59, 0.72, 0.79, 0.84}},
     {MfmaTile::KSplit, tiles::kKSplit[0], tiles::kKSplit[1], 2, {0.65, 0.78, 0, 0}},
     {MfmaTile::KSplit32, tiles::kKSplit32[0], tiles::kKSplit32[1], 4, {0.25, 0.30, 0.40, 0.50}},
+    {MfmaTile::WSplit, tiles::kWSplit[0], tiles::kWSplit[1], 2, {0.75, 0.82, 0, 0}},
 };
 
 }  // namespace
 
-MfmaTile choose_mfma_tile(int M, int N, int cus)
+// Whether the tile with its K range split over its four waves may take the
+// product. It runs two work-groups per compute unit, so a third tile per
+// compute unit waits for a second round, and the partial last chunk of a
+// ragged K (not a multiple of 32) costs each tile a load's round trip. Where
+// either counts, the 64x64 tiles that hold three or four per compute unit at
+// once were faster (interleaved medians on MI355X, TFLOP/s, split over waves
+// against plain 64x64: 1200 x 2400 x 1200 86.1 / 106.0, 1536 x 1500 x 1000
+// 70.4 / 82.7, 2200^3 99.5 / 112.2, 2200^2 x 2208 110.2 / 113.5), and with
+// one tile per compute unit or K a multiple of 32 and at most three tiles
+// per compute unit, slower (1000^3 96.6 / 74.5, 1536^3 95.7 / 90.6). A
+// product under 64 wide leaves most of the tile idle (16000 x 8 x 1000: 10.0
+// against 11.0 on the 32x32 tile).
+bool wsplit_fits(std::int64_t M, std::int64_t N, std::int64_t K, std::int64_t cus)
 {
+    if (M < 64 || N < 64) return false;
+    const std::int64_t m = ceil_div(ceil_div(M, 64) * ceil_div(N, 64), cus);
+    return m == 1 || (K % 32 == 0 && m <= 3);
+}
+
+MfmaTile choose_mfma_tile(int M, int N, int K, int cus)
+{
+#if defined(SGEMM_MFMA_FORCE_TILE)
+    // Tile sweeps: every product takes the shape numbered here (MfmaTile).
+    (void)M;
+    (void)N;
+    (void)K;
+    (void)cus;
+    return static_cast<MfmaTile>(SGEMM_MFMA_FORCE_TILE);
+#endif
     const std::int64_t n_cus = cus > 0 ? cus : 256;
     MfmaTile best = MfmaTile::Big;
     double best_t = -1.0;
     for (const Candidate &c : kCandidates) {  // ties go to the earlier (larger or simpler) shape
+        if (c.tile == MfmaTile::WSplit && !wsplit_fits(M, N, K, n_cus)) continue;
         const double t = launch_time(c, M, N, n_cus);
         if (best_t < 0.0 || t < best_t) {
             best_t = t;
@@ -148,7 +185,7 @@ SplitChoice choose_split(int M, int N, int K, int cus)
     constexpr int kMaxCus = 1 << 16;  // no device has more; keeps the grid (CUs x slots) in range
     if (n_cus > kMaxCus) return none;
     // Whole tiles: the chosen shape's estimated time.
-    const MfmaTile dp_tile = choose_mfma_tile(M, N, n_cus);
+    const MfmaTile dp_tile = choose_mfma_tile(M, N, K, n_cus);
     const Candidate *dp = &kCandidates[0];
     for (const Candidate &c : kCandidates)
         if (c.tile == dp_tile) dp = &c;
@@ -209,13 +246,13 @@ extern "C" int sgemm_regblock_tile(int M, int N, int cus)
     return sgemm_impl::regblock_tile_size(M, N, cus);
 }
 
-extern "C" int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN)
+extern "C" int sgemm_mfma_tile(int M, int N, int K, int cus, int *BM, int *BN)
 {
     using namespace sgemm_impl;
-    if (M < 0 || N < 0) return SGEMM_ERR_DIM;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
     if (BM == nullptr || BN == nullptr) return SGEMM_ERR_NULL;
     const int *dims = tiles::kSmall;
-    switch (choose_mfma_tile(M, N, cus)) {
+    switch (choose_mfma_tile(M, N, K, cus)) {
     case MfmaTile::Big: dims = tiles::kBig; break;
     case MfmaTile::Mid: dims = tiles::kMid; break;
     case MfmaTile::Small: dims = tiles::kSmall; break;
@@ -224,6 +261,7 @@ extern "C" int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN)
     case MfmaTile::WideN: dims = tiles::kWideN; break;
     case MfmaTile::MidDual: dims = tiles::kMidDual; break;
     case MfmaTile::KSplit32: dims = tiles::kKSplit32; break;
+    case MfmaTile::WSplit: dims = tiles::kWSplit; break;
     }
     *BM = dims[0];
     *BN = dims[1];
@@ -242,14 +280,14 @@ extern "C" std::size_t sgemm_ex_workspace_size(int transA, int transB, int M, in
     return c.use ? c.bytes : 0;
 }
 
-extern "C" int sgemm_mfma_shape(int M, int N, int cus, int *shape)
+extern "C" int sgemm_mfma_shape(int M, int N, int K, int cus, int *shape)
 {
     using namespace sgemm_impl;
-    if (M < 0 || N < 0) return SGEMM_ERR_DIM;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
     if (shape == nullptr) return SGEMM_ERR_NULL;
     const int *dims = tiles::kSmall;
     int sets = 1;
-    switch (choose_mfma_tile(M, N, cus)) {
+    switch (choose_mfma_tile(M, N, K, cus)) {
     case MfmaTile::Big: dims = tiles::kBig; break;
     case MfmaTile::Mid: dims = tiles::kMid; break;
     case MfmaTile::Small: dims = tiles::kSmall; break;
@@ -260,6 +298,10 @@ extern "C" int sgemm_mfma_shape(int M, int N, int cus, int *shape)
     case MfmaTile::KSplit32:
         dims = tiles::kKSplit32;
         sets = tiles::kKSplit32[5];
+        break;
+    case MfmaTile::WSplit:
+        dims = tiles::kWSplit;
+        sets = tiles::kWSplit[5];
         break;
     case MfmaTile::Wide: dims = tiles::kWide; break;
     case MfmaTile::WideN: dims = tiles::kWideN; break;

@@ -7,9 +7,10 @@
 
 namespace sgemm_impl {
 
-// The interior tile shape with the smallest estimated time for an M x N
-// product on `cus` compute units (cus <= 0 means 256, an MI355X).
-MfmaTile choose_mfma_tile(int M, int N, int cus);
+// The interior tile shape with the smallest estimated time for an M x N x K
+// product on `cus` compute units (cus <= 0 means 256, an MI355X). K matters
+// only to the 64x64 tile whose K range is split over its waves.
+MfmaTile choose_mfma_tile(int M, int N, int K, int cus);
 
 // The split ("stream-K") schedule for an M x N x K product: whether its
 // estimated time beats the whole-tile launch, the tile shape and work-group

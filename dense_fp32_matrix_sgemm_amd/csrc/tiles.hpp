@@ -98,10 +98,17 @@
 #define SGEMM_MFMA_KSPLIT32_TILE 32, 32, 32, 1, 1, 2
 #endif
 
+// Tile rows per band of the tile order (tile_io.hpp: tile_of_index).
+#ifndef SGEMM_MFMA_GROUP_M
+#define SGEMM_MFMA_GROUP_M 8
+#endif
+
 namespace sgemm_impl {
 
-// Interior tile shape of one matrix-core launch.
-enum class MfmaTile { Big, Mid, Small, KSplit, Wide, WideN, MidDual, KSplit32 };
+// Interior tile shape of one matrix-core launch. WSplit is the 64 x 64 tile
+// whose K range is split over its four waves, each holding the whole tile
+// (wsplit.hpp).
+enum class MfmaTile { Big, Mid, Small, KSplit, Wide, WideN, MidDual, KSplit32, WSplit };
 
 namespace tiles {
 constexpr int kGeneral[] = {SGEMM_MFMA_TILE};
@@ -113,6 +120,8 @@ constexpr int kWide[] = {SGEMM_MFMA_WIDE_TILE};
 constexpr int kWideN[] = {SGEMM_MFMA_WIDEN_TILE};
 constexpr int kMidDual[] = {SGEMM_MFMA_MID_DUAL_TILE};
 constexpr int kKSplit32[] = {SGEMM_MFMA_KSPLIT32_TILE};
+// BM, BN, k per chunk, 1 x 1 waves per set, 4 sets (each wave one set).
+constexpr int kWSplit[] = {64, 64, 32, 1, 1, 4};
 }  // namespace tiles
 
 }  // namespace sgemm_impl

@@ -362,26 +362,31 @@ int sgemm_best_variant(int M, int N, int K);
 int sgemm_regblock_tile(int M, int N, int cus);
 
 /*
- * The interior tile (BM x BN) the MFMA variant uses for an M x N product on
- * a device with `cus` compute units (cus <= 0: 256, an MI355X); tiles are
+ * The interior tile (BM x BN) the MFMA variant uses for an M x N x K product
+ * on a device with `cus` compute units (cus <= 0: 256, an MI355X); tiles are
  * tuned per problem as section 07 and exercise 2 of "Matrix Multiplication --
  * Naive to Tiled" describe. The choice estimates each shape's launch time
  * from how its work-groups fall into rounds over the compute units and the
- * throughput measured for that shape, and takes the fastest. Pure host
- * logic: no HIP call. Returns SGEMM_OK, SGEMM_ERR_DIM (M or N negative) or
- * SGEMM_ERR_NULL (BM or BN NULL).
+ * throughput measured for that shape, and takes the fastest; K counts only
+ * for the 64 x 64 tile whose K range is split over its waves (taken for a K
+ * that is not a multiple of 32 only with one tile per compute unit). Pure
+ * host logic: no HIP call. Returns SGEMM_OK, SGEMM_ERR_DIM (M, N or K
+ * negative) or SGEMM_ERR_NULL (BM or BN NULL).
  */
-int sgemm_mfma_tile(int M, int N, int cus, int *BM, int *BN);
+int sgemm_mfma_tile(int M, int N, int K, int cus, int *BM, int *BN);
 
 /*
  * The whole kernel shape behind sgemm_mfma_tile's choice, in shape[0..5]:
- * BM, BN, BK (slab depth), the waves per work-group along M and N, and the
- * number of wave sets that split each slab's k between them (1, or 2 for the
- * 64 x 64 tile that puts two waves on each SIMD when one such tile per
- * compute unit would leave one). Pure host logic. Returns SGEMM_OK,
- * SGEMM_ERR_DIM or SGEMM_ERR_NULL (shape NULL).
+ * BM, BN, BK (slab depth; for the split tile below, the k per chunk), the
+ * waves per work-group along M and N, and the number of wave sets that
+ * split the K range between them: 1; 2 for the 64 x 64 and 32 x 32 tiles
+ * whose two sets share each slab, which put two waves on each SIMD where one
+ * tile per compute unit would leave one; 4 for the 64 x 64 tile whose four
+ * waves each hold the whole tile over a quarter of K's chunks (1 x 1 waves
+ * per set). Pure host logic. Returns SGEMM_OK, SGEMM_ERR_DIM or
+ * SGEMM_ERR_NULL (shape NULL).
  */
-int sgemm_mfma_shape(int M, int N, int cus, int *shape);
+int sgemm_mfma_shape(int M, int N, int K, int cus, int *shape);
 
 #ifdef __cplusplus
 }

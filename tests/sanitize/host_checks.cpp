@@ -88,20 +88,22 @@ int main()
     for (int M : sizes)
         for (int N : sizes)
             for (int cus : cus_list) {
-                int bm = -1, bn = -1;
-                const int rt = sgemm_mfma_tile(M, N, cus, &bm, &bn);
-                expect(is_status(rt), "sgemm_mfma_tile status", M, N, cus);
-                if (rt == SGEMM_OK)
-                    expect(((bm == 32 || bm == 64 || bm == 128 || bm == 256) && bn == bm) || (bm == 192 && bn == 128) ||
-                               (bm == 128 && bn == 192),
-                           "tile", M, N, bm);
-                int shape[6] = {-1, -1, -1, -1, -1, -1};
-                const int rs = sgemm_mfma_shape(M, N, cus, shape);
-                expect(is_status(rs), "sgemm_mfma_shape status", M, N, cus);
-                if (rs == SGEMM_OK)
-                    expect(shape[0] > 0 && shape[1] > 0 && shape[2] > 0 && shape[3] > 0 && shape[4] > 0 &&
-                               (shape[5] == 1 || shape[5] == 2),
-                           "shape", M, N, cus);
+                for (int K : sizes) {
+                    int bm = -1, bn = -1;
+                    const int rt = sgemm_mfma_tile(M, N, K, cus, &bm, &bn);
+                    expect(is_status(rt), "sgemm_mfma_tile status", M, N, cus);
+                    if (rt == SGEMM_OK)
+                        expect(((bm == 32 || bm == 64 || bm == 128 || bm == 256) && bn == bm) ||
+                                   (bm == 192 && bn == 128) || (bm == 128 && bn == 192),
+                               "tile", M, N, bm);
+                    int shape[6] = {-1, -1, -1, -1, -1, -1};
+                    const int rs = sgemm_mfma_shape(M, N, K, cus, shape);
+                    expect(is_status(rs), "sgemm_mfma_shape status", M, N, cus);
+                    if (rs == SGEMM_OK)
+                        expect(shape[0] > 0 && shape[1] > 0 && shape[2] > 0 && shape[3] > 0 && shape[4] > 0 &&
+                                   (shape[5] == 1 || shape[5] == 2 || shape[5] == 4),
+                               "shape", M, N, cus);
+                }
                 for (int K : sizes) {
                     const std::size_t w = sgemm_ex_workspace_size(0, 1, M, N, K, cus);
                     if (M <= 0 || N <= 0 || K <= 0) expect(w == 0, "no workspace for an empty product", M, N, K);

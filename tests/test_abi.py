@@ -216,53 +216,81 @@ def test_matmul_rejects_bad_tensors():
 
 def test_mfma_tile_choice(lib):
     # One 256x256 tile per compute unit at 4096^2; 128x128 when 256x256 tiles
-    # would leave most compute units idle (2048^2); 64x64, several resident
-    # per compute unit, for the ragged shape and small products.
-    assert sg.sgemm_mfma_tile(4096, 4096) == (256, 256)
-    assert sg.sgemm_mfma_tile(8192, 8192) == (256, 256)
-    assert sg.sgemm_mfma_tile(2048, 2048) == (128, 128)
-    assert sg.sgemm_mfma_tile(1024, 1024) == (64, 64)
-    assert sg.sgemm_mfma_tile(3001, 2047) == (192, 128)   # 16 x 16 tiles: one per compute unit
-    assert sg.sgemm_mfma_tile(3072, 2048) == (192, 128)
-    assert sg.sgemm_mfma_tile(2047, 3001) == (128, 192)   # the same, turned round
-    assert sg.sgemm_mfma_tile(2048, 3072) == (128, 192)
-    assert sg.sgemm_mfma_tile(128, 128) == (32, 32)     # at most one 32 x 32 tile per compute unit
-    assert sg.sgemm_mfma_tile(512, 512) == (32, 32)
-    assert sg.sgemm_mfma_tile(640, 640) == (64, 64)     # two 32 x 32 tiles per compute unit
+    # would leave most compute units idle (2048^2); 64x64 for the mid sizes
+    # and 32x32 for the smallest products.
+    assert sg.sgemm_mfma_tile(4096, 4096, 4096) == (256, 256)
+    assert sg.sgemm_mfma_tile(8192, 8192, 8192) == (256, 256)
+    assert sg.sgemm_mfma_tile(2048, 2048, 2048) == (128, 128)
+    assert sg.sgemm_mfma_tile(1024, 1024, 1024) == (64, 64)
+    assert sg.sgemm_mfma_tile(3001, 2047, 4093) == (192, 128)   # 16 x 16 tiles: one per compute unit
+    assert sg.sgemm_mfma_tile(3072, 2048, 4096) == (192, 128)
+    assert sg.sgemm_mfma_tile(2047, 3001, 4093) == (128, 192)   # the same, turned round
+    assert sg.sgemm_mfma_tile(2048, 3072, 4096) == (128, 192)
+    assert sg.sgemm_mfma_tile(128, 128, 128) == (32, 32)     # at most one 32 x 32 tile per compute unit
+    assert sg.sgemm_mfma_tile(512, 512, 512) == (32, 32)
+    assert sg.sgemm_mfma_tile(640, 640, 640) == (64, 64)     # two 32 x 32 tiles per compute unit
     # Fewer compute units shift the choice toward larger tiles.
-    assert sg.sgemm_mfma_tile(2048, 2048, cus=64) == (256, 256)
-    assert sg.sgemm_mfma_tile(4096, 4096, cus=0) == sg.sgemm_mfma_tile(4096, 4096, cus=256)
+    assert sg.sgemm_mfma_tile(2048, 2048, 2048, cus=64) == (256, 256)
+    assert sg.sgemm_mfma_tile(4096, 4096, 4096, cus=0) == sg.sgemm_mfma_tile(4096, 4096, 4096, cus=256)
+
+
+WSPLIT = (64, 64, 32, 1, 1, 4)    # K split over four waves, each holding the whole tile
+KSPLIT32 = (32, 32, 32, 1, 1, 2)  # two single-wave sets sharing each slab
+SMALL = (64, 64, 16, 2, 2, 1)     # plain 64x64, up to four work-groups per compute unit
 
 
 def test_mfma_shape_choice(lib):
-    # One 64x64 tile per compute unit takes the two-set K-split tile (two
-    # waves per SIMD); several resident per compute unit, the plain one.
-    assert sg.sgemm_mfma_shape(1024, 1024) == (64, 64, 32, 2, 2, 2)
-    assert sg.sgemm_mfma_shape(1000, 1000) == (64, 64, 32, 2, 2, 2)
-    assert sg.sgemm_mfma_shape(128, 128) == (32, 32, 32, 1, 1, 2)
-    assert sg.sgemm_mfma_shape(300, 257) == (32, 32, 32, 1, 1, 2)
-    assert sg.sgemm_mfma_shape(3001, 2047) == (192, 128, 16, 2, 2, 1)
-    assert sg.sgemm_mfma_shape(2047, 3001) == (128, 192, 16, 2, 2, 1)
-    assert sg.sgemm_mfma_shape(4096, 4096) == (256, 256, 16, 4, 2, 1)
-    assert sg.sgemm_mfma_shape(2048, 2048) == (128, 128, 32, 2, 4, 1)
+    # One 64x64 tile per compute unit takes the tile whose K range is split
+    # over its four waves, whatever K; up to three per compute unit too when K
+    # is a multiple of 32 (its chunk), else the 64x64 tiles that hold three or
+    # four per compute unit at once. Products that leave most compute units
+    # without a 64x64 tile, or under 64 wide, take the 32x32 tile.
+    assert sg.sgemm_mfma_shape(1024, 1024, 1024) == WSPLIT
+    assert sg.sgemm_mfma_shape(1000, 1000, 1000) == WSPLIT
+    assert sg.sgemm_mfma_shape(640, 640, 640) == WSPLIT
+    assert sg.sgemm_mfma_shape(1536, 1536, 1536) == WSPLIT
+    assert sg.sgemm_mfma_shape(2048, 1024, 1024) == WSPLIT
+    assert sg.sgemm_mfma_shape(4000, 70, 4000) == WSPLIT
+    assert sg.sgemm_mfma_shape(1024, 1024, 1) == WSPLIT
+    # Ragged K with two or more tiles per compute unit.
+    assert sg.sgemm_mfma_shape(2048, 1024, 1000) != WSPLIT
+    assert sg.sgemm_mfma_shape(1536, 1500, 1000) != WSPLIT
+    assert sg.sgemm_mfma_shape(1200, 2400, 1200) != WSPLIT
+    assert sg.sgemm_mfma_shape(1536, 1500, 1024) == WSPLIT
+    # More than three tiles per compute unit.
+    assert sg.sgemm_mfma_shape(2200, 2200, 2208) != WSPLIT
+    assert sg.sgemm_mfma_shape(2560, 2560, 2560) == SMALL
+    # Under 64 wide.
+    assert sg.sgemm_mfma_shape(16000, 8, 1000) != WSPLIT
+    assert sg.sgemm_mfma_shape(16384, 5, 64) != WSPLIT
+    assert sg.sgemm_mfma_shape(512, 512, 512) == KSPLIT32
+    assert sg.sgemm_mfma_shape(128, 128, 128) == KSPLIT32
+    assert sg.sgemm_mfma_shape(300, 257, 513) == KSPLIT32
+    assert sg.sgemm_mfma_shape(3001, 2047, 4093) == (192, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(2047, 3001, 4093) == (128, 192, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(4096, 4096, 4096) == (256, 256, 16, 4, 2, 1)
+    assert sg.sgemm_mfma_shape(2048, 2048, 2048) == (128, 128, 32, 2, 4, 1)
     # Two or more 128 x 128 tiles per compute unit: the four-wave tile, two
     # work-groups to a compute unit; one per compute unit: the eight-wave one.
-    assert sg.sgemm_mfma_shape(2048, 4096) == (128, 128, 16, 2, 2, 1)
-    assert sg.sgemm_mfma_shape(4000, 5000) == (128, 128, 16, 2, 2, 1)
-    assert sg.sgemm_mfma_shape(16384, 512) == (128, 128, 16, 2, 2, 1)
-    assert sg.sgemm_mfma_shape(8192, 512) == (128, 128, 32, 2, 4, 1)
-    for shape in [(7, 9), (128, 128), (1024, 1024), (3001, 2047), (4096, 4096), (8192, 300), (2048, 4096)]:
+    assert sg.sgemm_mfma_shape(2048, 4096, 2048) == (128, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(4000, 5000, 2000) == (128, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(16384, 512, 4096) == (128, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(8192, 512, 4096) == (128, 128, 32, 2, 4, 1)
+    for shape in [(7, 9, 5), (128, 128, 128), (1024, 1024, 1024), (3001, 2047, 4093), (4096, 4096, 4096),
+                  (8192, 300, 100), (2048, 4096, 2048), (1536, 1500, 1000)]:
         assert sg.sgemm_mfma_shape(*shape)[:2] == sg.sgemm_mfma_tile(*shape)
     shp = (ctypes.c_int * 6)()
-    assert lib.sgemm_mfma_shape(-1, 4, 0, shp) == sg.SGEMM_ERR_DIM
-    assert lib.sgemm_mfma_shape(4, 4, 0, None) == sg.SGEMM_ERR_NULL
+    assert lib.sgemm_mfma_shape(-1, 4, 4, 0, shp) == sg.SGEMM_ERR_DIM
+    assert lib.sgemm_mfma_shape(4, 4, -1, 0, shp) == sg.SGEMM_ERR_DIM
+    assert lib.sgemm_mfma_shape(4, 4, 4, 0, None) == sg.SGEMM_ERR_NULL
 
 
 def test_mfma_tile_errors(lib):
     bm, bn = ctypes.c_int(), ctypes.c_int()
-    assert lib.sgemm_mfma_tile(-1, 4, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_ERR_DIM
-    assert lib.sgemm_mfma_tile(4, 4, 0, None, ctypes.byref(bn)) == sg.SGEMM_ERR_NULL
-    assert lib.sgemm_mfma_tile(0, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_OK
+    assert lib.sgemm_mfma_tile(-1, 4, 4, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_ERR_DIM
+    assert lib.sgemm_mfma_tile(4, 4, -1, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_ERR_DIM
+    assert lib.sgemm_mfma_tile(4, 4, 4, 0, None, ctypes.byref(bn)) == sg.SGEMM_ERR_NULL
+    assert lib.sgemm_mfma_tile(0, 0, 0, 0, ctypes.byref(bm), ctypes.byref(bn)) == sg.SGEMM_OK
 
 
 def test_regblock_tile_choice(lib):

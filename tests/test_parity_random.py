@@ -135,7 +135,7 @@ LARGE_CASES = _large_cases(8096, 24)
 @pytest.mark.parametrize("case", LARGE_CASES, ids=_id)
 def test_random_large_fp32(case, workspace):
     i, M, N, K, tA, tB, alpha, beta, pads, offs = case
-    print(f"[random] large fp32 {_id(case)} tile {sg.sgemm_mfma_tile(M, N)} alpha {alpha} beta {beta} pads {pads} "
+    print(f"[random] large fp32 {_id(case)} tile {sg.sgemm_mfma_tile(M, N, K)} alpha {alpha} beta {beta} pads {pads} "
           f"offsets {offs}", flush=True)
     opA = synth.uniform_pm1(3 * i + 301, (M, K))
     opB = synth.uniform_pm1(3 * i + 302, (K, N))

@@ -6,9 +6,12 @@ walks slabs of 32 staged through two register sets, two slabs per pass of its
 unrolled loop, and the four-wave 192x128, 128x192 and 128x128 tiles slabs of
 16 the same way. A product runs its whole slabs through the pipelined loop
 (the steady state needs three or more, the last ones run without loads) and
-the partial last slab, if any, separately. These tests
-take K on both sides of every such boundary, up to three whole slabs plus a
-partial one, for every transpose pair:
+the partial last slab, if any, separately. The 64x64 tile whose K range is
+split over its four waves deals chunks of 32 out to the waves in turn (wave
+c mod 4 takes chunk c, two per pass of its loop) and gives the partial last
+chunk to wave (K div 32) mod 4. These tests take K on both sides of every
+such boundary, up to three whole slabs plus a partial one (up to nine chunks
+for the split tile), for every transpose pair:
 - small-integer operands, where every partial sum is exact and the whole of C
   must equal the integer product bit for bit;
 - uniform operands with alpha and beta against the oracle on sampled outputs,
@@ -29,21 +32,28 @@ pytestmark = pytest.mark.gpu
 
 PAIRS = [(False, False), (False, True), (True, False), (True, True)]
 
-# (M, N), the tile (BM, BN, BK) the library picks for it, and the K values
-# around its slab boundaries: 1, under and over one slab, two, three, four,
-# five and six.
-TILES = [((1536, 1500), (64, 64, 16)), ((1000, 1000), (64, 64, 32)), ((3001, 2047), (192, 128, 16)),
-         ((2047, 3001), (128, 192, 16)), ((2000, 2040), (128, 128, 32)), ((2040, 4001), (128, 128, 16)),
-         ((300, 257), (32, 32, 32))]
+WSPLIT = (64, 64, 32, 1, 1, 4)
+KSPLIT = (64, 64, 32, 2, 2, 2)
+# (M, N), the slab depth whose boundaries K walks around, the kernel shape
+# the library picks (BM, BN, BK, waves along M and N, wave sets), and the one
+# it picks instead when K is a multiple of 32, if different: 2048 x 1024
+# holds two 64x64 tiles per compute unit and takes the tile split over its
+# waves when K is whole chunks, the two-set tile otherwise.
+TILES = [((2560, 2530), 16, (64, 64, 16, 2, 2, 1), None), ((1000, 1000), 32, WSPLIT, None),
+         ((2048, 1024), 32, KSPLIT, WSPLIT), ((3001, 2047), 16, (192, 128, 16, 2, 2, 1), None),
+         ((2047, 3001), 16, (128, 192, 16, 2, 2, 1), None), ((2000, 2040), 32, (128, 128, 32, 2, 4, 1), None),
+         ((2040, 4001), 16, (128, 128, 16, 2, 2, 1), None), ((300, 257), 32, (32, 32, 32, 1, 1, 2), None)]
 
 
-def _ks(tile):
-    bk = tile[2]
-    return sorted({1, bk // 2, bk - 1, bk, bk + 1, 2 * bk - 1, 2 * bk, 2 * bk + 1, 3 * bk, 3 * bk + 1, 4 * bk - 1,
-                   4 * bk + 5, 5 * bk + 3, 6 * bk})
+def _ks(bk):
+    ks = {1, bk // 2, bk - 1, bk, bk + 1, 2 * bk - 1, 2 * bk, 2 * bk + 1, 3 * bk, 3 * bk + 1, 4 * bk - 1,
+          4 * bk + 5, 5 * bk + 3, 6 * bk}
+    if bk == 32:  # the split tile's chunks: two and more per wave, a partial ninth
+        ks |= {8 * bk - 1, 8 * bk, 8 * bk + 1, 9 * bk + 7}
+    return sorted(ks)
 
 
-CASES = [(mn, tile, k) for mn, tile in TILES for k in _ks(tile)]
+CASES = [(mn, shape if alt is None or k % 32 else alt, k) for mn, bk, shape, alt in TILES for k in _ks(bk)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -60,8 +70,8 @@ def _stored(x, trans):
 @pytest.mark.parametrize("mn,tile,K", CASES, ids=[f"{m}x{n}x{k}" for (m, n), _, k in CASES])
 def test_slab_boundaries(mn, tile, K):
     M, N = mn
-    shape = sg.sgemm_mfma_shape(M, N)
-    assert shape[:3] == tile, shape
+    shape = sg.sgemm_mfma_shape(M, N, K)
+    assert shape == tile, shape
     for tA, tB in PAIRS:
         print(f"[slabs] {M}x{N}x{K} tile {shape} pair {(tA, tB)}", flush=True)
         Ai = synth.small_int(K + 31, (M, K))
