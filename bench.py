@@ -65,7 +65,7 @@ PEAK_HBM_GBS = 8000.0
 
 METRIC = "FP32 SGEMM TFLOP/s at 4096^3 on 1 MI355X; % of FP32 peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mfma_sq4096_traffic.json")
-KERNEL_SOURCES = ["mfma.hpp", "mfma_nn.hip", "tile_io.hpp", "gemm.hpp", "tiles.hpp", "select.cpp"]
+KERNEL_SOURCES = ["mfma.hpp", "wsplit.hpp", "mfma_nn.hip", "tile_io.hpp", "gemm.hpp", "tiles.hpp", "select.cpp"]
 
 
 def flops(M: int, N: int, K: int) -> int:
@@ -258,8 +258,9 @@ def oracle_seconds_one_thread(M: int, N: int, K: int, dist: str) -> float:
     return float(r.stdout.strip().splitlines()[-1])
 
 
-def all_configs(lib, sg, dev) -> dict:
-    """Every variant on every configuration: timing, sampled check, oracle."""
+def all_configs(lib, sg, dev, only=None) -> dict:
+    """Every variant on every configuration (or the variants named in
+    `only`): timing, sampled check, oracle."""
     import numpy as np
     import torch
 
@@ -280,6 +281,8 @@ def all_configs(lib, sg, dev) -> dict:
         ref, sabs = oracle.gemm_entries(A, B, rows, cols)
         entry = {"M": M, "N": N, "K": K, "values": dist, "variants": {}}
         for name in ALL_CONFIG_VARIANTS:
+            if only is not None and name not in only:
+                continue
             code = sg.VARIANTS[name]
 
             def call(code=code):
@@ -425,6 +428,9 @@ def main(argv=None) -> int:
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the headline, time every variant on every configuration "
                          "and the CPU oracle on each")
+    ap.add_argument("--only", default=None,
+                    help="with --all-configs: comma-separated variants to run (default: all of " +
+                         ", ".join(ALL_CONFIG_VARIANTS) + ")")
     ap.add_argument("--cold", action="store_true",
                     help="instead of the headline line, time the product with the caches flushed "
                          "(a 512 MiB write) before every launch, next to the same launches back to back")
@@ -467,7 +473,14 @@ def main(argv=None) -> int:
         return 0
 
     if args.all_configs:
-        print(json.dumps({"metric": METRIC, "all_configs": all_configs(lib, sg, dev)}), flush=True)
+        only = None
+        if args.only:
+            only = set(args.only.split(","))
+            unknown = only - set(ALL_CONFIG_VARIANTS)
+            if unknown:
+                print(f"--only: unknown variants {sorted(unknown)}", file=sys.stderr)
+                return 2
+        print(json.dumps({"metric": METRIC, "all_configs": all_configs(lib, sg, dev, only)}), flush=True)
         return 0
 
     M = N = K = args.size
