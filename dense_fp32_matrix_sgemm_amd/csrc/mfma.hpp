@@ -1083,6 +1083,9 @@ using WideCfg = MfmaConfig<SGEMM_MFMA_WIDE_TILE, SGEMM_MFMA_WIDE_REG_SETS>;
 using WideNCfg = MfmaConfig<SGEMM_MFMA_WIDEN_TILE, SGEMM_MFMA_WIDEN_REG_SETS>;
 using KSplitCfg = KSplitConfig<SGEMM_MFMA_KSPLIT_TILE, SGEMM_MFMA_KSPLIT_REG_SETS>;
 using KSplit32Cfg = KSplitConfig<SGEMM_MFMA_KSPLIT32_TILE, SGEMM_MFMA_KSPLIT_REG_SETS>;
+using Ws64Cfg = WsConfig<SGEMM_MFMA_WSPLIT64>;
+using Ws96Cfg = WsConfig<SGEMM_MFMA_WSPLIT96>;
+using Ws128Cfg = WsConfig<SGEMM_MFMA_WSPLIT128>;
 
 // Products too small for a single interior tile: general tiles only.
 template <class Cfg, bool TA, bool TB, bool VEC>
@@ -1285,11 +1288,18 @@ hipError_t launch_by_shape(const Problem &p, hipStream_t stream)
     case MfmaTile::WideN: return launch_tiles<WideNCfg, TA, TB>(p, stream);
     case MfmaTile::KSplit: return launch_ksplit<KSplitCfg, TA, TB>(p, stream);
     case MfmaTile::KSplit32: return launch_ksplit<KSplit32Cfg, TA, TB>(p, stream);
+    // The tiles whose K range is split over their waves form buffer offsets
+    // in 31 bits; larger operands take the LDS-staged tile of the same size
+    // (two-set 64x64, eight-wave 128x128 for both larger ones).
     case MfmaTile::WSplit:
-        // Buffer offsets are formed in 31 bits; larger operands take the
-        // two-set 64 x 64 tile.
-        if (wsplit_offsets_fit(p)) return launch_wsplit<TA, TB>(p, stream);
+        if (wsplit_offsets_fit<Ws64Cfg>(p)) return launch_wsplit<Ws64Cfg, TA, TB>(p, stream);
         return launch_ksplit<KSplitCfg, TA, TB>(p, stream);
+    case MfmaTile::WSplit96:
+        if (wsplit_offsets_fit<Ws96Cfg>(p)) return launch_wsplit<Ws96Cfg, TA, TB>(p, stream);
+        return launch_tiles<MidCfg, TA, TB>(p, stream);
+    case MfmaTile::WSplit128:
+        if (wsplit_offsets_fit<Ws128Cfg>(p)) return launch_wsplit<Ws128Cfg, TA, TB>(p, stream);
+        return launch_tiles<MidCfg, TA, TB>(p, stream);
     case MfmaTile::Small: break;
     }
     return launch_tiles<SmallCfg, TA, TB>(p, stream);

@@ -37,7 +37,12 @@
 // 94.4, 768^3 54.9 -> 58.6, 2048 x 1024 x 1024 116.0 -> 121.0, 1536^3 90.3
 // -> 95.9); it loses where it gives most compute units no tile at all
 // (512 x 512 x 4096: 49.4 on the 32x32 tile, 31.9 on it), and where a compute
-// unit holds three or more (2048^3: 116 against 135 for 128x128).
+// unit holds three or more (2048^3: 116 against 135 for 128x128). The same
+// split on 96x96 and 128x128 tiles, one work-group per compute unit, runs at
+// 0.89 and 0.95 where a compute unit holds one (1536^3 89.7 -> 131.3,
+// 1536 x 1536 x 4096 92.3 -> 143.0, 2048^3 135.4 -> 143.1, 2048^2 x 4096
+// 138.9 -> 147.7, 1920^3 119.6 -> 125.5; forced where it would hold more,
+// 96x96 at 2048^3 117 and 128x128 at 1536^3 80).
 //
 // Pure C++ (no HIP), so it is tested on the host.
 #include <cstddef>
@@ -78,27 +83,41 @@ const Candidate kCandidates[] = {
     {MfmaTile::KSplit, tiles::kKSplit[0], tiles::kKSplit[1], 2, {0.65, 0.78, 0, 0}},
     {MfmaTile::KSplit32, tiles::kKSplit32[0], tiles::kKSplit32[1], 4, {0.25, 0.30, 0.40, 0.50}},
     {MfmaTile::WSplit, tiles::kWSplit[0], tiles::kWSplit[1], 2, {0.75, 0.82, 0, 0}},
+    {MfmaTile::WSplit96, tiles::kWSplit96[0], tiles::kWSplit96[1], 1, {0.89, 0, 0, 0}},
+    {MfmaTile::WSplit128, tiles::kWSplit128[0], tiles::kWSplit128[1], 1, {0.95, 0, 0, 0}},
 };
 
 }  // namespace
 
-// Whether the tile with its K range split over its four waves may take the
-// product. It runs two work-groups per compute unit, so a third tile per
+// Whether the 64x64 tile with its K range split over its four waves may take
+// the product. It runs two work-groups per compute unit, so a third tile per
 // compute unit waits for a second round, and the partial last chunk of a
 // ragged K (not a multiple of 32) costs each tile a load's round trip. Where
-// either counts, the 64x64 tiles that hold three or four per compute unit at
+// both count, the 64x64 tiles that hold three or four per compute unit at
 // once were faster (interleaved medians on MI355X, TFLOP/s, split over waves
 // against plain 64x64: 1200 x 2400 x 1200 86.1 / 106.0, 1536 x 1500 x 1000
-// 70.4 / 82.7, 2200^3 99.5 / 112.2, 2200^2 x 2208 110.2 / 113.5), and with
-// one tile per compute unit or K a multiple of 32 and at most three tiles
-// per compute unit, slower (1000^3 96.6 / 74.5, 1536^3 95.7 / 90.6). A
-// product under 64 wide leaves most of the tile idle (16000 x 8 x 1000: 10.0
-// against 11.0 on the 32x32 tile).
+// 70.4 / 82.7), and so they were with more than three per compute unit
+// (2200^3 99.5 / 112.2, 2200^2 x 2208 110.2 / 113.5); with up to two per
+// compute unit whatever K, or three with K a multiple of 32, this tile was
+// faster (1000^3 96.6 / 74.5, 1536^3 95.7 / 90.6, 1200^3 80.3 / 77.6 before,
+// 2048 x 1024 x 1000 118.0 / 109.3 on the two-set tile, 80 x 12000 x 1000
+// 55.6 / 50.7). A product under 64 wide leaves most of the tile idle (16000
+// x 8 x 1000: 10.0 against 11.0 on the 32x32 tile).
 bool wsplit_fits(std::int64_t M, std::int64_t N, std::int64_t K, std::int64_t cus)
 {
     if (M < 64 || N < 64) return false;
     const std::int64_t m = ceil_div(ceil_div(M, 64) * ceil_div(N, 64), cus);
-    return m == 1 || (K % 32 == 0 && m <= 3);
+    return m <= 2 || (K % 32 == 0 && m <= 3);
+}
+
+// The 96x96 and 128x128 tiles split over their waves run one work-group per
+// compute unit: taken only where a compute unit holds a single one, and not
+// for products narrower than the tile.
+bool wsplit_large_fits(std::int64_t M, std::int64_t N, std::int64_t K, std::int64_t edge, std::int64_t cus)
+{
+    (void)K;
+    if (M < edge || N < edge) return false;
+    return ceil_div(M, edge) * ceil_div(N, edge) <= cus;
 }
 
 MfmaTile choose_mfma_tile(int M, int N, int K, int cus)
@@ -116,6 +135,9 @@ MfmaTile choose_mfma_tile(int M, int N, int K, int cus)
     double best_t = -1.0;
     for (const Candidate &c : kCandidates) {  // ties go to the earlier (larger or simpler) shape
         if (c.tile == MfmaTile::WSplit && !wsplit_fits(M, N, K, n_cus)) continue;
+        if ((c.tile == MfmaTile::WSplit96 || c.tile == MfmaTile::WSplit128) &&
+            !wsplit_large_fits(M, N, K, c.bm, n_cus))
+            continue;
         const double t = launch_time(c, M, N, n_cus);
         if (best_t < 0.0 || t < best_t) {
             best_t = t;
@@ -262,6 +284,8 @@ extern "C" int sgemm_mfma_tile(int M, int N, int K, int cus, int *BM, int *BN)
     case MfmaTile::MidDual: dims = tiles::kMidDual; break;
     case MfmaTile::KSplit32: dims = tiles::kKSplit32; break;
     case MfmaTile::WSplit: dims = tiles::kWSplit; break;
+    case MfmaTile::WSplit96: dims = tiles::kWSplit96; break;
+    case MfmaTile::WSplit128: dims = tiles::kWSplit128; break;
     }
     *BM = dims[0];
     *BN = dims[1];
@@ -302,6 +326,14 @@ extern "C" int sgemm_mfma_shape(int M, int N, int K, int cus, int *shape)
     case MfmaTile::WSplit:
         dims = tiles::kWSplit;
         sets = tiles::kWSplit[5];
+        break;
+    case MfmaTile::WSplit96:
+        dims = tiles::kWSplit96;
+        sets = tiles::kWSplit96[5];
+        break;
+    case MfmaTile::WSplit128:
+        dims = tiles::kWSplit128;
+        sets = tiles::kWSplit128[5];
         break;
     case MfmaTile::Wide: dims = tiles::kWide; break;
     case MfmaTile::WideN: dims = tiles::kWideN; break;

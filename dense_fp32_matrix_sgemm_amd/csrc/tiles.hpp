@@ -105,10 +105,26 @@
 
 namespace sgemm_impl {
 
-// Interior tile shape of one matrix-core launch. WSplit is the 64 x 64 tile
-// whose K range is split over its four waves, each holding the whole tile
-// (wsplit.hpp).
-enum class MfmaTile { Big, Mid, Small, KSplit, Wide, WideN, MidDual, KSplit32, WSplit };
+// The tiles whose K range is split over their four waves, each wave holding
+// the whole tile (wsplit.hpp): blocks of 32 x 32 per side (tile edge 64, 96,
+// 128), k per chunk, register sets a wave's chunks stream through, and the
+// waves per SIMD its registers are bounded for. The 64 x 64 tile keeps two
+// sets within 256 registers, so two work-groups can share a compute unit;
+// the larger ones take a compute unit each (their partial tiles fill most of
+// the LDS anyway).
+#ifndef SGEMM_MFMA_WSPLIT64
+#define SGEMM_MFMA_WSPLIT64 2, 32, 2, 2
+#endif
+#ifndef SGEMM_MFMA_WSPLIT96
+#define SGEMM_MFMA_WSPLIT96 3, 32, 2, 1
+#endif
+#ifndef SGEMM_MFMA_WSPLIT128
+#define SGEMM_MFMA_WSPLIT128 4, 16, 2, 1
+#endif
+
+// Interior tile shape of one matrix-core launch. WSplit, WSplit96 and
+// WSplit128 are the tiles whose K range is split over their waves.
+enum class MfmaTile { Big, Mid, Small, KSplit, Wide, WideN, MidDual, KSplit32, WSplit, WSplit96, WSplit128 };
 
 namespace tiles {
 constexpr int kGeneral[] = {SGEMM_MFMA_TILE};
@@ -121,7 +137,12 @@ constexpr int kWideN[] = {SGEMM_MFMA_WIDEN_TILE};
 constexpr int kMidDual[] = {SGEMM_MFMA_MID_DUAL_TILE};
 constexpr int kKSplit32[] = {SGEMM_MFMA_KSPLIT32_TILE};
 // BM, BN, k per chunk, 1 x 1 waves per set, 4 sets (each wave one set).
-constexpr int kWSplit[] = {64, 64, 32, 1, 1, 4};
+constexpr int kWs64[] = {SGEMM_MFMA_WSPLIT64};
+constexpr int kWs96[] = {SGEMM_MFMA_WSPLIT96};
+constexpr int kWs128[] = {SGEMM_MFMA_WSPLIT128};
+constexpr int kWSplit[] = {32 * kWs64[0], 32 * kWs64[0], kWs64[1], 1, 1, 4};
+constexpr int kWSplit96[] = {32 * kWs96[0], 32 * kWs96[0], kWs96[1], 1, 1, 4};
+constexpr int kWSplit128[] = {32 * kWs128[0], 32 * kWs128[0], kWs128[1], 1, 1, 4};
 }  // namespace tiles
 
 }  // namespace sgemm_impl

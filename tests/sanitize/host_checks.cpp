@@ -93,7 +93,7 @@ int main()
                     const int rt = sgemm_mfma_tile(M, N, K, cus, &bm, &bn);
                     expect(is_status(rt), "sgemm_mfma_tile status", M, N, cus);
                     if (rt == SGEMM_OK)
-                        expect(((bm == 32 || bm == 64 || bm == 128 || bm == 256) && bn == bm) ||
+                        expect(((bm == 32 || bm == 64 || bm == 96 || bm == 128 || bm == 256) && bn == bm) ||
                                    (bm == 192 && bn == 128) || (bm == 128 && bn == 192),
                                "tile", M, N, bm);
                     int shape[6] = {-1, -1, -1, -1, -1, -1};

@@ -235,28 +235,41 @@ def test_mfma_tile_choice(lib):
 
 
 WSPLIT = (64, 64, 32, 1, 1, 4)    # K split over four waves, each holding the whole tile
+WSPLIT96 = (96, 96, 32, 1, 1, 4)  # the same on 96x96 and 128x128 tiles, one work-group per compute unit
+WSPLIT128 = (128, 128, 16, 1, 1, 4)
+MID = (128, 128, 32, 2, 4, 1)     # eight waves staged through LDS
 KSPLIT32 = (32, 32, 32, 1, 1, 2)  # two single-wave sets sharing each slab
 SMALL = (64, 64, 16, 2, 2, 1)     # plain 64x64, up to four work-groups per compute unit
 
 
 def test_mfma_shape_choice(lib):
-    # One 64x64 tile per compute unit takes the tile whose K range is split
-    # over its four waves, whatever K; up to three per compute unit too when K
-    # is a multiple of 32 (its chunk), else the 64x64 tiles that hold three or
-    # four per compute unit at once. Products that leave most compute units
-    # without a 64x64 tile, or under 64 wide, take the 32x32 tile.
+    # Up to two 64x64 tiles per compute unit take the tile whose K range is
+    # split over its four waves, whatever K; three too when K is a multiple of
+    # 32 (its chunk), else the 64x64 tiles that hold three or four per compute
+    # unit at once. Products that leave most compute units without a 64x64
+    # tile, or under 64 wide, take the 32x32 tile; under 64 rows with two
+    # 64x64 tiles per compute unit, the two-set 64x64 tile.
     assert sg.sgemm_mfma_shape(1024, 1024, 1024) == WSPLIT
     assert sg.sgemm_mfma_shape(1000, 1000, 1000) == WSPLIT
     assert sg.sgemm_mfma_shape(640, 640, 640) == WSPLIT
-    assert sg.sgemm_mfma_shape(1536, 1536, 1536) == WSPLIT
+    # One 96x96 or 128x128 tile per compute unit: the larger split tiles.
+    assert sg.sgemm_mfma_shape(1536, 1536, 1536) == WSPLIT96
+    assert sg.sgemm_mfma_shape(1500, 1500, 1500) == WSPLIT96
+    assert sg.sgemm_mfma_shape(2048, 2048, 2048) == WSPLIT128
+    assert sg.sgemm_mfma_shape(2000, 2040, 77) == WSPLIT128
+    assert sg.sgemm_mfma_shape(8192, 512, 4096) == WSPLIT128
+    # Under 128 rows, the eight-wave 128x128 tile.
+    assert sg.sgemm_mfma_shape(120, 30000, 100) == MID
+    assert sg.sgemm_mfma_shape(48, 12000, 1000) == (64, 64, 32, 2, 2, 2)
     assert sg.sgemm_mfma_shape(2048, 1024, 1024) == WSPLIT
     assert sg.sgemm_mfma_shape(4000, 70, 4000) == WSPLIT
     assert sg.sgemm_mfma_shape(1024, 1024, 1) == WSPLIT
-    # Ragged K with two or more tiles per compute unit.
-    assert sg.sgemm_mfma_shape(2048, 1024, 1000) != WSPLIT
-    assert sg.sgemm_mfma_shape(1536, 1500, 1000) != WSPLIT
-    assert sg.sgemm_mfma_shape(1200, 2400, 1200) != WSPLIT
-    assert sg.sgemm_mfma_shape(1536, 1500, 1024) == WSPLIT
+    # Ragged K: up to two 64x64 tiles per compute unit, not three.
+    assert sg.sgemm_mfma_shape(2048, 1024, 1000) == WSPLIT
+    assert sg.sgemm_mfma_shape(1200, 1200, 1200) == WSPLIT
+    assert sg.sgemm_mfma_shape(1200, 2400, 1200) == SMALL
+    assert sg.sgemm_mfma_shape(1536, 1500, 1000) == WSPLIT96
+    assert sg.sgemm_mfma_shape(1536, 1500, 1024) == WSPLIT96
     # More than three tiles per compute unit.
     assert sg.sgemm_mfma_shape(2200, 2200, 2208) != WSPLIT
     assert sg.sgemm_mfma_shape(2560, 2560, 2560) == SMALL
@@ -269,13 +282,11 @@ def test_mfma_shape_choice(lib):
     assert sg.sgemm_mfma_shape(3001, 2047, 4093) == (192, 128, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(2047, 3001, 4093) == (128, 192, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(4096, 4096, 4096) == (256, 256, 16, 4, 2, 1)
-    assert sg.sgemm_mfma_shape(2048, 2048, 2048) == (128, 128, 32, 2, 4, 1)
     # Two or more 128 x 128 tiles per compute unit: the four-wave tile, two
     # work-groups to a compute unit; one per compute unit: the eight-wave one.
     assert sg.sgemm_mfma_shape(2048, 4096, 2048) == (128, 128, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(4000, 5000, 2000) == (128, 128, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(16384, 512, 4096) == (128, 128, 16, 2, 2, 1)
-    assert sg.sgemm_mfma_shape(8192, 512, 4096) == (128, 128, 32, 2, 4, 1)
     for shape in [(7, 9, 5), (128, 128, 128), (1024, 1024, 1024), (3001, 2047, 4093), (4096, 4096, 4096),
                   (8192, 300, 100), (2048, 4096, 2048), (1536, 1500, 1000)]:
         assert sg.sgemm_mfma_shape(*shape)[:2] == sg.sgemm_mfma_tile(*shape)

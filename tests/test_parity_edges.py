@@ -5,8 +5,8 @@ others, with their reads clamped into the operands and the partial chunk of
 a row-contiguous operand read from a shifted address and rotated into place.
 These tests run ragged products whose chosen tile shape (each of 256x256,
 192x128, 128x192, both 128x128 tiles, 64x64, the 64x64 and 32x32 tiles
-whose slabs two wave sets share, and the 64x64 tile whose K range is split
-over its four waves) leaves
+whose slabs two wave sets share, and the 64x64, 96x96 and 128x128 tiles whose
+K range is split over their four waves) leaves
 partial tiles on both edges, for every transpose pair, with alpha and beta,
 and the narrowest widths the clamped reads allow (4 to 7) next to the general
 path below them. Every comparison is with the
@@ -42,24 +42,30 @@ def _stored(x, trans):
 
 # (M, N, K) and the kernel shape the library picks for it (BM, BN, BK, waves
 # along M and N, wave sets; checked on the host):
-# - 1000^3 and 1001 x 999 x 1000 hold one 64x64 tile per compute unit and
-#   take the tile whose K range is split over its four waves, with a partial
-#   last chunk (1000 = 31 * 32 + 8) and, at odd widths, pairs shifted at the
-#   right edge (B as given) or bottom edge (A transposed); so do 4001 x 67 x
-#   320 and 70 x 4000 x 4000, 67 and 70 wide, and 1500 x 1100 x 320 with two
-#   tiles per compute unit;
-# - 2040 x 1000 x 1000 and 1500 x 1100 x 333 hold two per compute unit with a
-#   ragged K and take the two-set 64x64 tile;
+# - the tiles whose K range is split over their four waves: 1000^3, 1001 x 999
+#   x 1000, 4001 x 67 x 320 and 70 x 4000 x 4000 hold one 64x64 tile per
+#   compute unit, 1500 x 1100 x 320 and 2040 x 1000 x 1000 two (1000 = 31 *
+#   32 + 8: a partial last chunk); 1501 x 1499 x 333 and 1499 x 1501 x 1000
+#   one 96x96 tile, 2001 x 2047 x 77, 2046 x 2045 x 100 and 1900 x 2100 x 77
+#   one 128x128; their odd widths shift the groups read at the right edge (B
+#   as given) or bottom edge (A transposed) by 1, 2 or 3;
+# - 60 x 12000 x 333 (under 64 rows) takes the two-set 64x64 tile, 120 x 30000
+#   x 77 (under 128) the eight-wave 128x128 tile;
 # - 4300^2 and 2001 x 4095 hold two or more 128x128 tiles per compute unit and
 #   take the four-wave one; 300 x 257 and 37 x 45 take the 32x32 tile whose
 #   slabs two single waves share; 2560 x 2530 the plain 64x64 tile.
 WSPLIT = (64, 64, 32, 1, 1, 4)
+WSPLIT96 = (96, 96, 32, 1, 1, 4)
+WSPLIT128 = (128, 128, 16, 1, 1, 4)
 KSPLIT = (64, 64, 32, 2, 2, 2)
+MID = (128, 128, 32, 2, 4, 1)
 RAGGED = [((5000, 3000, 333), (256, 256, 16, 4, 2, 1)), ((4300, 4300, 130), (128, 128, 16, 2, 2, 1)),
           ((3001, 2047, 4093), (192, 128, 16, 2, 2, 1)), ((2047, 3001, 4093), (128, 192, 16, 2, 2, 1)),
-          ((1900, 2100, 77), (128, 128, 32, 2, 4, 1)), ((1000, 1000, 1000), WSPLIT), ((1001, 999, 1000), WSPLIT),
-          ((4001, 67, 320), WSPLIT), ((70, 4000, 4000), WSPLIT), ((1500, 1100, 320), WSPLIT),
-          ((2040, 1000, 1000), KSPLIT), ((1500, 1100, 333), KSPLIT), ((2560, 2530, 100), (64, 64, 16, 2, 2, 1)),
+          ((1900, 2100, 77), WSPLIT128), ((2001, 2047, 77), WSPLIT128), ((2046, 2045, 100), WSPLIT128),
+          ((1501, 1499, 333), WSPLIT96), ((1499, 1501, 1000), WSPLIT96), ((1000, 1000, 1000), WSPLIT),
+          ((1001, 999, 1000), WSPLIT), ((4001, 67, 320), WSPLIT), ((70, 4000, 4000), WSPLIT),
+          ((1500, 1100, 320), WSPLIT), ((2040, 1000, 1000), WSPLIT), ((60, 12000, 333), KSPLIT),
+          ((120, 30000, 77), MID), ((2560, 2530, 100), (64, 64, 16, 2, 2, 1)),
           ((2900, 1910, 515), (192, 128, 16, 2, 2, 1)), ((2040, 3001, 515), (128, 192, 16, 2, 2, 1)),
           ((2001, 4095, 1001), (128, 128, 16, 2, 2, 1)), ((300, 257, 513), (32, 32, 32, 1, 1, 2)),
           ((37, 45, 77), (32, 32, 32, 1, 1, 2))]

@@ -33,27 +33,33 @@ pytestmark = pytest.mark.gpu
 PAIRS = [(False, False), (False, True), (True, False), (True, True)]
 
 WSPLIT = (64, 64, 32, 1, 1, 4)
+WSPLIT96 = (96, 96, 32, 1, 1, 4)
+WSPLIT128 = (128, 128, 16, 1, 1, 4)
 KSPLIT = (64, 64, 32, 2, 2, 2)
-# (M, N), the slab depth whose boundaries K walks around, the kernel shape
-# the library picks (BM, BN, BK, waves along M and N, wave sets), and the one
-# it picks instead when K is a multiple of 32, if different: 2048 x 1024
-# holds two 64x64 tiles per compute unit and takes the tile split over its
-# waves when K is whole chunks, the two-set tile otherwise.
-TILES = [((2560, 2530), 16, (64, 64, 16, 2, 2, 1), None), ((1000, 1000), 32, WSPLIT, None),
-         ((2048, 1024), 32, KSPLIT, WSPLIT), ((3001, 2047), 16, (192, 128, 16, 2, 2, 1), None),
-         ((2047, 3001), 16, (128, 192, 16, 2, 2, 1), None), ((2000, 2040), 32, (128, 128, 32, 2, 4, 1), None),
-         ((2040, 4001), 16, (128, 128, 16, 2, 2, 1), None), ((300, 257), 32, (32, 32, 32, 1, 1, 2), None)]
+MID = (128, 128, 32, 2, 4, 1)
+# (M, N), the slab or chunk depth whose boundaries K walks around, and the
+# kernel shape the library picks (BM, BN, BK, waves along M and N, wave
+# sets): the tiles split over their waves at 1000^2 (one 64x64 tile per
+# compute unit), 2048 x 1024 (two), 1500^2 (one 96x96) and 2000 x 2040 (one
+# 128x128); under 64 rows the two-set 64x64 tile, under 128 the eight-wave
+# 128x128 tile.
+TILES = [((2560, 2530), 16, (64, 64, 16, 2, 2, 1)), ((1000, 1000), 32, WSPLIT), ((2048, 1024), 32, WSPLIT),
+         ((1500, 1500), 32, WSPLIT96), ((2000, 2040), 16, WSPLIT128), ((48, 12000), 32, KSPLIT),
+         ((120, 30000), 32, MID), ((3001, 2047), 16, (192, 128, 16, 2, 2, 1)),
+         ((2047, 3001), 16, (128, 192, 16, 2, 2, 1)), ((2040, 4001), 16, (128, 128, 16, 2, 2, 1)),
+         ((300, 257), 32, (32, 32, 32, 1, 1, 2))]
+SPLIT = {WSPLIT, WSPLIT96, WSPLIT128}
 
 
-def _ks(bk):
+def _ks(bk, shape):
     ks = {1, bk // 2, bk - 1, bk, bk + 1, 2 * bk - 1, 2 * bk, 2 * bk + 1, 3 * bk, 3 * bk + 1, 4 * bk - 1,
           4 * bk + 5, 5 * bk + 3, 6 * bk}
-    if bk == 32:  # the split tile's chunks: two and more per wave, a partial ninth
+    if shape in SPLIT:  # the split tiles' chunks: two and more per wave, a partial ninth
         ks |= {8 * bk - 1, 8 * bk, 8 * bk + 1, 9 * bk + 7}
     return sorted(ks)
 
 
-CASES = [(mn, shape if alt is None or k % 32 else alt, k) for mn, bk, shape, alt in TILES for k in _ks(bk)]
+CASES = [(mn, shape, k) for mn, bk, shape in TILES for k in _ks(bk, shape)]
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -59,7 +59,7 @@ def _sampled_check(tA, tB, alpha, A, B, beta, C0, C, what):
 
 # (M, N, K): ragged edges with a K tail, an exact fit, a deep-K thin product
 # and a square one, all put on the split schedule by the library.
-SHAPES = [(2047, 2560, 4093), (2560, 2560, 2560), (1000, 1000, 8000), (1536, 1536, 1536), (517, 509, 16001)]
+SHAPES = [(2047, 2560, 4093), (2560, 2560, 2560), (1000, 1000, 8000), (3072, 3072, 3072), (517, 509, 16001)]
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=PAIR_IDS)
