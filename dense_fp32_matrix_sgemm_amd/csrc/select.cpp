@@ -39,7 +39,7 @@
 // (512 x 512 x 4096: 49.4 on the 32x32 tile, 31.9 on it), and where a compute
 // unit holds three or more (2048^3: 116 against 135 for 128x128). The same
 // split on 96x96 and 128x128 tiles, one work-group per compute unit, runs at
-// 0.89 and 0.95 where a compute unit holds one (1536^3 89.7 -> 131.3,
+// 0.89 and 1.02 where it is taken (1536^3 89.7 -> 131.3,
 // 1536 x 1536 x 4096 92.3 -> 143.0, 2048^3 135.4 -> 143.1, 2048^2 x 4096
 // 138.9 -> 147.7, 1920^3 119.6 -> 125.5; forced where it would hold more,
 // 96x96 at 2048^3 117 and 128x128 at 1536^3 80).
@@ -84,7 +84,7 @@ const Candidate kCandidates[] = {
     {MfmaTile::KSplit32, tiles::kKSplit32[0], tiles::kKSplit32[1], 4, {0.25, 0.30, 0.40, 0.50}},
     {MfmaTile::WSplit, tiles::kWSplit[0], tiles::kWSplit[1], 2, {0.75, 0.82, 0, 0}},
     {MfmaTile::WSplit96, tiles::kWSplit96[0], tiles::kWSplit96[1], 1, {0.89, 0, 0, 0}},
-    {MfmaTile::WSplit128, tiles::kWSplit128[0], tiles::kWSplit128[1], 1, {0.95, 0, 0, 0}},
+    {MfmaTile::WSplit128, tiles::kWSplit128[0], tiles::kWSplit128[1], 1, {1.02, 0, 0, 0}},
 };
 
 }  // namespace
@@ -111,13 +111,24 @@ bool wsplit_fits(std::int64_t M, std::int64_t N, std::int64_t K, std::int64_t cu
 }
 
 // The 96x96 and 128x128 tiles split over their waves run one work-group per
-// compute unit: taken only where a compute unit holds a single one, and not
-// for products narrower than the tile.
+// compute unit, so a compute unit's tiles run one after another, each paying
+// its first loads and its sum of partial tiles with nothing to overlap them
+// (about 7 us a tile; the 128x128 tile's loop runs at 0.98 of peak against
+// 0.95 for the 256x256 tile). So they are taken where a compute unit holds a
+// single one; the 128x128 tile also where K >= 2048 and its tiles fill every
+// round of the compute units to 95% or more (4096^3 147.5 -> 150.3,
+// 6144^2 x 4096 147.3 -> 150.3, 8192^2 x 4096 147.9 -> 150.7, 16384 x 512 x
+// 4096 142.4 -> 148.3, 2048 x 4096 x 2048 141.5 -> 145.3; not at 4096^2 x
+// 1024, 138.0 against 140.4, 5000 x 3000 x 2000, 94% full, 122.9 against
+// 125.0, or 3072^3, 75%, 112 against 127). Not for products narrower than
+// the tile.
 bool wsplit_large_fits(std::int64_t M, std::int64_t N, std::int64_t K, std::int64_t edge, std::int64_t cus)
 {
-    (void)K;
     if (M < edge || N < edge) return false;
-    return ceil_div(M, edge) * ceil_div(N, edge) <= cus;
+    const std::int64_t tiles = ceil_div(M, edge) * ceil_div(N, edge);
+    const std::int64_t m = ceil_div(tiles, cus);
+    if (m == 1) return true;
+    return edge == 128 && K >= 2048 && tiles * 20 >= m * cus * 19;
 }
 
 MfmaTile choose_mfma_tile(int M, int N, int K, int cus)

@@ -215,11 +215,14 @@ def test_matmul_rejects_bad_tensors():
 
 
 def test_mfma_tile_choice(lib):
-    # One 256x256 tile per compute unit at 4096^2; 128x128 when 256x256 tiles
-    # would leave most compute units idle (2048^2); 64x64 for the mid sizes
-    # and 32x32 for the smallest products.
-    assert sg.sgemm_mfma_tile(4096, 4096, 4096) == (256, 256)
-    assert sg.sgemm_mfma_tile(8192, 8192, 8192) == (256, 256)
+    # 128x128 tiles split over their waves where they fill whole rounds of
+    # the compute units with K >= 2048 (4096^3: four rounds) or give one per
+    # compute unit (2048^2); 256x256 tiles at 4096^2 with a short K; 64x64
+    # for the mid sizes and 32x32 for the smallest products.
+    assert sg.sgemm_mfma_tile(4096, 4096, 4096) == (128, 128)
+    assert sg.sgemm_mfma_tile(8192, 8192, 8192) == (128, 128)
+    assert sg.sgemm_mfma_tile(4096, 4096, 1024) == (256, 256)
+    assert sg.sgemm_mfma_tile(5000, 3000, 2000) == (256, 256)
     assert sg.sgemm_mfma_tile(2048, 2048, 2048) == (128, 128)
     assert sg.sgemm_mfma_tile(1024, 1024, 1024) == (64, 64)
     assert sg.sgemm_mfma_tile(3001, 2047, 4093) == (192, 128)   # 16 x 16 tiles: one per compute unit
@@ -230,7 +233,7 @@ def test_mfma_tile_choice(lib):
     assert sg.sgemm_mfma_tile(512, 512, 512) == (32, 32)
     assert sg.sgemm_mfma_tile(640, 640, 640) == (64, 64)     # two 32 x 32 tiles per compute unit
     # Fewer compute units shift the choice toward larger tiles.
-    assert sg.sgemm_mfma_tile(2048, 2048, 2048, cus=64) == (256, 256)
+    assert sg.sgemm_mfma_tile(2048, 2048, 1024, cus=64) == (256, 256)
     assert sg.sgemm_mfma_tile(4096, 4096, 4096, cus=0) == sg.sgemm_mfma_tile(4096, 4096, 4096, cus=256)
 
 
@@ -281,12 +284,18 @@ def test_mfma_shape_choice(lib):
     assert sg.sgemm_mfma_shape(300, 257, 513) == KSPLIT32
     assert sg.sgemm_mfma_shape(3001, 2047, 4093) == (192, 128, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(2047, 3001, 4093) == (128, 192, 16, 2, 2, 1)
-    assert sg.sgemm_mfma_shape(4096, 4096, 4096) == (256, 256, 16, 4, 2, 1)
+    assert sg.sgemm_mfma_shape(4096, 4096, 4096) == WSPLIT128
+    assert sg.sgemm_mfma_shape(6144, 6144, 4096) == WSPLIT128
+    assert sg.sgemm_mfma_shape(4096, 4096, 1024) == (256, 256, 16, 4, 2, 1)    # short K
+    assert sg.sgemm_mfma_shape(3072, 3072, 3072) == SMALL                      # rounds 75% full
     # Two or more 128 x 128 tiles per compute unit: the four-wave tile, two
     # work-groups to a compute unit; one per compute unit: the eight-wave one.
-    assert sg.sgemm_mfma_shape(2048, 4096, 2048) == (128, 128, 16, 2, 2, 1)
+    # (unless the split 128x128 tile fills whole rounds with K >= 2048).
+    assert sg.sgemm_mfma_shape(2048, 4096, 1024) == (128, 128, 16, 2, 2, 1)
     assert sg.sgemm_mfma_shape(4000, 5000, 2000) == (128, 128, 16, 2, 2, 1)
-    assert sg.sgemm_mfma_shape(16384, 512, 4096) == (128, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(16384, 512, 1024) == (128, 128, 16, 2, 2, 1)
+    assert sg.sgemm_mfma_shape(2048, 4096, 2048) == WSPLIT128
+    assert sg.sgemm_mfma_shape(16384, 512, 4096) == WSPLIT128
     for shape in [(7, 9, 5), (128, 128, 128), (1024, 1024, 1024), (3001, 2047, 4093), (4096, 4096, 4096),
                   (8192, 300, 100), (2048, 4096, 2048), (1536, 1500, 1000)]:
         assert sg.sgemm_mfma_shape(*shape)[:2] == sg.sgemm_mfma_tile(*shape)
